@@ -1,0 +1,247 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (100M-token bank on one GPU): 195,313 documents x 512 tokens,
+pool 64 -> 1,562,504 pooled rows.  The pooled router keys (8 heads x 128,
+bf16, 3.2 GB) are resident in HBM; the pooled content K/V (8 x 128, bf16,
+6.4 GB) are in pinned host memory.  One step is one pass of the whole hot
+path on fresh synthetic inputs:
+  1. pool: msa_pool_encode of a batch of 64 new documents x 512 tokens
+     (document-wise RoPE + chunk means of K/V/Kr);
+  2. route: msa_route with one query token - cosine scan of the whole bank,
+     head mean, per-document max, top-16, then the host-driven copy of the
+     16 selected documents' pooled K/V from pinned memory;
+  3. decode: msa_sparse_decode, GQA 32/8 x 128 over [128 memory rows ;
+     4096 local tokens] with the query offset by k = 16.
+Inputs are resident before the timed region.  Prints one JSON line.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_latent_memory_amd as msa  # noqa: E402
+from sparse_latent_memory_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E peak, GB/s
+
+
+class HipEvents:
+    """Plain hipEvent_t pairs from the HIP runtime torch has loaded."""
+
+    def __init__(self, n):
+        lib_dir = os.path.join(os.path.dirname(torch.__file__), "lib")
+        self.hip = ctypes.CDLL(os.path.join(lib_dir, "libamdhip64.so"))
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a, b))
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float()
+        a, b = self.pairs[i]
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--latency-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the bank is held whole in one GPU's HBM); "
+              "multi-GPU runs are not supported", file=sys.stderr)
+        sys.exit(2)
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    msa.load()
+    cfg = synth.config(4)
+    K, W = args.steps, args.warmup
+    n_steps = W + K + args.latency_steps
+
+    # ---------------- resident inputs ----------------
+    t_setup = time.time()
+    lens = synth.doc_lengths(cfg)
+    pool_off = synth.row_offsets(lens, cfg.pool)
+    n_docs, n_pool = len(lens), int(pool_off[-1])
+    bank_tokens = int(lens.sum())
+    log(f"bank: {n_docs} docs, {bank_tokens} tokens, {n_pool} pooled rows")
+    kr = synth.pooled_router_bank(cfg, lens, device=dev)
+    host_kv = synth.pooled_content_bank(cfg, lens, device=dev, pin=True)
+    pool_off_d = torch.as_tensor(pool_off, device=dev)
+    pool_off_h = torch.as_tensor(pool_off)
+    enc = synth.config(4, n_docs=64)
+    enc_lens = synth.doc_lengths(enc)
+    enc_bank = synth.raw_bank(enc, lens=enc_lens, device=dev)
+    enc_pool_off = synth.row_offsets(enc_lens, enc.pool)
+    enc_pool_off_d = torch.as_tensor(enc_pool_off, device=dev)
+    enc_npool = int(enc_pool_off[-1])
+    enc_kv = torch.empty((enc_npool, 2, cfg.n_kv_heads, cfg.head_dim), dtype=cfg.torch_dtype, device=dev)
+    enc_kr = torch.empty((enc_npool, cfg.n_router_heads, cfg.router_dim), dtype=cfg.torch_dtype, device=dev)
+    lk, lv = synth.local_context(cfg, device=dev)
+    qrs = [synth.router_queries(cfg, step=i, device=dev) for i in range(n_steps)]
+    qs = [synth.decode_queries(cfg, step=i, device=dev) for i in range(n_steps)]
+    k = cfg.top_k
+    mem_cap = k * (512 // cfg.pool)
+    copy_stream = torch.cuda.Stream()
+    asm = msa.Assembly.allocate(host_kv, pool_off_h, cfg.batch, k, mem_cap, dev, copy_stream=copy_stream)
+    loc_len = torch.full((cfg.batch,), cfg.local_len, dtype=torch.int32, device=dev)
+    pos = torch.full((cfg.batch,), k, dtype=torch.int32, device=dev)
+    rws = torch.empty(msa.route_workspace_bytes(cfg.torch_dtype, cfg.batch, 1, cfg.n_router_heads, cfg.router_dim,
+                                                n_docs, n_pool, k), dtype=torch.uint8, device=dev)
+    dws = torch.empty(msa.decode_workspace_bytes(cfg.batch, cfg.n_q_heads, cfg.head_dim, mem_cap, cfg.local_len),
+                      dtype=torch.uint8, device=dev)
+    doc_scores = torch.empty((cfg.batch, n_docs), dtype=torch.float32, device=dev)
+    topk_idx = torch.empty((cfg.batch, k), dtype=torch.int32, device=dev)
+    topk_score = torch.empty((cfg.batch, k), dtype=torch.float32, device=dev)
+    out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=cfg.torch_dtype, device=dev)
+    lse = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f} s")
+
+    scan_ev = HipEvents(K)
+    dec_ev = HipEvents(K)
+    stream = torch.cuda.current_stream()
+
+    def step(i, j=None):
+        msa.pool_encode(enc_bank["k"], enc_bank["v"], enc_bank["kr"], enc_bank["doc_tok_off"], enc_pool_off_d,
+                        enc.pool, enc.rope_theta, enc_npool, enc_kv, enc_kr, stream=stream)
+        msa.route(qrs[i], kr, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=asm, stream=stream,
+                  prof_events=None if j is None else scan_ev.pairs[j])
+        msa.sparse_decode(qs[i], asm.mem_kv, asm.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
+                          stream=stream, prof_events=None if j is None else dec_ev.pairs[j])
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done")
+    t0 = time.perf_counter()
+    for j in range(K):
+        step(W + j, j)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    log(f"timed {K} steps: {elapsed * 1e3 / K:.3f} ms/step")
+
+    scan_ms = np.array([scan_ev.elapsed_ms(j) for j in range(K)])
+    dec_ms = np.array([dec_ev.elapsed_ms(j) for j in range(K)])
+
+    # route + decode latency per step (synchronised each step)
+    lat = []
+    for i in range(W + K, n_steps):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        msa.route(qrs[i], kr, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=asm, stream=stream)
+        msa.sparse_decode(qs[i], asm.mem_kv, asm.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
+                          stream=stream)
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - a) * 1e3)
+    lat = np.array(lat)
+
+    scan_bytes = n_pool * cfg.n_router_heads * cfg.router_dim * 2 + cfg.n_router_heads * cfg.router_dim * 2
+    scan_avg_s = scan_ms.mean() / 1e3
+    achieved = scan_bytes / scan_avg_s / 1e9
+    value = cfg.batch * bank_tokens * K / elapsed
+    dec_bytes = (mem_cap + cfg.local_len) * cfg.n_kv_heads * cfg.head_dim * 2 * 2
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, kr, pool_off, qrs[W], args.cpu_seconds)
+
+    res = {
+        "metric": "bank tokens scored/s (% HBM peak); p50 route+decode step at 100M bank",
+        "value": value,
+        "unit": "bank tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": elapsed * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "bank-100M-decode: 195,313 docs x 512 tokens, pool 64 -> 1,562,504 pooled rows; "
+                        "Kr 8x128 bf16 in HBM (3.2 GB); pooled K/V 8x128 bf16 in pinned host memory (6.4 GB); "
+                        "1 query token, top-16, gather, decode GQA 32/8x128 over 128 memory rows + 4096 local "
+                        "tokens; plus a 64-doc x 512-token encode batch per step",
+            "bank_tokens": bank_tokens,
+            "pooled_rows": n_pool,
+            "global_batch": cfg.batch,
+        },
+        "roofline": {
+            "kernel": "route bank scan (scan_mfma_kernel<8,4>)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "scan_us": scan_ms.mean() * 1e3,
+            "scan_bytes": scan_bytes,
+        },
+        "latency_ms": {
+            "route_decode_p50": float(np.percentile(lat, 50)),
+            "route_decode_p90": float(np.percentile(lat, 90)),
+            "route_decode_p99": float(np.percentile(lat, 99)),
+            "decode_attention_us": float(dec_ms.mean() * 1e3),
+            "decode_achieved_GBs": float(dec_bytes / (dec_ms.mean() / 1e3) / 1e9),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, kr, pool_off, qr, seconds):
+    """The float64 CPU oracle's routing on a bounded sample of the same bank:
+    consecutive blocks of 2048 documents from the start of the bank, scored
+    until `seconds` of CPU time have passed."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    qn = qr.detach().cpu().float().double().numpy()
+    block = 2048
+    done_docs, spent = 0, 0.0
+    n_docs = len(pool_off) - 1
+    while spent < seconds and done_docs < n_docs:
+        d0, d1 = done_docs, min(done_docs + block, n_docs)
+        rows = kr[pool_off[d0]:pool_off[d1]].float().cpu().double().numpy()
+        t = time.perf_counter()
+        oracle.doc_scores(qn, rows, pool_off[d0:d1 + 1] - pool_off[d0])
+        spent += time.perf_counter() - t
+        done_docs = d1
+    tokens = done_docs * 512
+    return {"value": tokens * cfg.batch / spent, "unit": "bank tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle.doc_scores (NumPy float64) over the first {done_docs} documents "
+                      f"({tokens} bank tokens, {int(pool_off[done_docs])} pooled rows) of the same bank, "
+                      f"one query token, in blocks of {block} documents; {spent:.1f} s of compute"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,241 @@
+/*
+ * msa.h - C ABI of libmsa, the MI355X (gfx950) hot path of Memory Sparse
+ * Attention (MSA).
+ *
+ * The three calls follow the method's three inference stages as described
+ * in "EverMind Releases Memory-Sparse Attention Code for Long-Context AI
+ * Models" (toolmesh.ai), section "Architectural Design and Inference", and
+ * in "EverMind-AI/MSA: Memory Sparse Attention for 100M-Token Contexts"
+ * (hysenlabs.com), section "How MSA compresses and routes documents":
+ *
+ *   msa_pool_encode   - offline memory encoding: chunk-mean pooling of each
+ *                       document's K / V / Kr, positions restarting per doc.
+ *   msa_route         - online routing and context assembly: cosine scores
+ *                       of the projected query Qr against the pooled router
+ *                       keys, mean over heads, max over tokens, max per
+ *                       document, top-k; optionally copies the selected
+ *                       documents' pooled K/V from pinned host memory.
+ *   msa_sparse_decode - sparse generation: one attention step over the
+ *                       assembled memory followed by the query's local K/V,
+ *                       with the query position offset by k.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Ownership: the caller owns every buffer (device memory, pinned host
+ *   memory from hipHostMalloc, workspaces).  The library allocates and
+ *   frees no memory.  Its only internal objects are per-thread HIP events.
+ * - Pointers marked "device" are device memory on the current HIP device;
+ *   "pinned host" pointers come from hipHostMalloc (or an equivalent pinned
+ *   allocation); "host" pointers are ordinary host memory.
+ * - Streams are hipStream_t values passed as void*; NULL is the default
+ *   stream.  Every call enqueues its work on `stream` and returns without
+ *   waiting, except msa_route with assembly (see there).
+ * - Dense row-major layouts; shapes are given outermost first.  Element
+ *   type of the float tensors is `dtype` (MSA_F32 or MSA_BF16); offsets are
+ *   int64, lengths and indices int32, scores fp32.
+ * - Errors: every argument is checked before anything is enqueued; a
+ *   non-zero return means nothing was enqueued (MSA_ERR_CAPACITY in
+ *   msa_route is the one documented exception).  Device-resident values
+ *   (offsets, lengths) cannot be checked on the host: kernels clamp every
+ *   index derived from them into the buffers they are given, so a bad value
+ *   yields wrong numbers, never an out-of-bounds access.  msa_last_error()
+ *   returns a thread-local message for the last non-OK return.  No C++
+ *   exception crosses the ABI.  Calls are re-entrant across threads.
+ * - Supported shapes: head_dim and router_dim in {64, 128}; n_q_heads a
+ *   multiple of n_kv_heads; 1 <= top_k <= min(n_docs, 4096).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, inconsistent shape  */
+  MSA_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim, top_k)  */
+  MSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+  MSA_ERR_CAPACITY = -4,    /* reserved; assembly drops what does not fit  */
+  MSA_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed  */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+/* ------------------------------------------------------------------------
+ * Stage 1 - offline memory encoding.
+ *
+ * For document d with L_d = doc_tok_off[d+1] - doc_tok_off[d] tokens and
+ * chunk c covering its tokens [c*P, min((c+1)*P, L_d)) (n_c tokens):
+ *   K_bar = mean over the chunk of RoPE(K_t, t - doc_tok_off[d])
+ *   V_bar = mean of V_t,   Kr_bar = mean of Kr_t
+ * written to pooled row doc_pool_off[d] + c.  RoPE is the rotate-half form:
+ * pair (j, j + D/2) of a head is rotated by angle p * theta^(-2j/D).
+ * Positions restart at zero in every document (document-wise RoPE, same
+ * sources as above; "Key Technical Details" of "MSA (Memory Sparse
+ * Attention) - An Open-Source Answer to AI's Memory Bottleneck").
+ * Only K is rotated; V and Kr are averaged as given.  Accumulation is fp32,
+ * the result is rounded to nearest-even into `dtype`.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;            /* msa_dtype of k, v, kr and both outputs       */
+  int32_t n_docs;           /* >= 1                                         */
+  int64_t n_tokens;         /* = doc_tok_off[n_docs]                        */
+  int64_t n_pool;           /* = doc_pool_off[n_docs]                       */
+  int32_t pool_size;        /* P >= 1                                       */
+  int32_t n_kv_heads;       /* Hkv >= 1                                     */
+  int32_t head_dim;         /* D in {64, 128}                               */
+  int32_t n_router_heads;   /* Hr >= 1                                      */
+  int32_t router_dim;       /* dr in {64, 128}                              */
+  int32_t reserved0;
+  double rope_theta;        /* > 0                                          */
+  const int64_t *doc_tok_off;  /* device [n_docs+1], non-decreasing, from 0 */
+  const int64_t *doc_pool_off; /* device [n_docs+1], prefix of ceil(L_d/P)  */
+  const void *k;            /* device [n_tokens, Hkv, D], K before RoPE     */
+  const void *v;            /* device [n_tokens, Hkv, D]                    */
+  const void *kr;           /* device [n_tokens, Hr, dr]                    */
+  void *kv_pooled;          /* device out [n_pool, 2, Hkv, D]: K_bar, V_bar */
+  void *kr_pooled;          /* device out [n_pool, Hr, dr]                  */
+} msa_pool_args;
+
+int msa_pool_encode(const msa_pool_args *args, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 2 - online routing and context assembly.
+ *
+ * For query b, token t, pooled row j:
+ *   s[b,t,j]  = (1/Hr) * sum_h cos(Qr[b,t,h], Kr_bar[j,h]),
+ *               cos(x, y) = <x,y> / (max(|x|,1e-8) * max(|y|,1e-8))
+ *   Dsc[b,d]  = max over t and over the rows j of document d of s[b,t,j]
+ *   top-k     = the k documents with the largest Dsc[b,.], ties to the
+ *               lower document id, in that order.
+ * Sources: as for stage 1 ("cosine similarity, mean-pooled across heads and
+ * then maxed over tokens, picks the Top-k documents" is restated there).
+ * doc_scores is always written.  Arithmetic: bf16 inputs are multiplied in
+ * the matrix cores with fp32 accumulation (the normalised query is split
+ * into two bf16 terms when at most 8 query tokens are routed at once);
+ * fp32 inputs use fp32 vector arithmetic.
+ *
+ * Assembly (when host_kv != NULL): the selected documents' pooled rows
+ * host_kv[doc_pool_off[d] .. doc_pool_off[d+1]) are copied, in rank order,
+ * into mem_kv[b, mem_len0[b] ...] where mem_len0[b] is host_mem_len[b] when
+ * `append` is set and 0 otherwise.  A document that does not fit in
+ * mem_cap rows is dropped together with every lower-ranked one.  This path
+ * BLOCKS the calling thread until the top-k indices are in host_topk_idx,
+ * then enqueues one hipMemcpyAsync per document on copy_stream, writes the
+ * new lengths to host_mem_len / host_mem_docs and copies them to mem_len,
+ * and makes `stream` wait for those copies (a later msa_sparse_decode on
+ * `stream` sees the assembled memory).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;            /* msa_dtype of qr and kr_pooled                */
+  int32_t batch;            /* B >= 1 independent queries                   */
+  int32_t q_tokens;         /* Tq >= 1 tokens per query                     */
+  int32_t n_router_heads;   /* Hr                                           */
+  int32_t router_dim;       /* dr in {64, 128}                              */
+  int32_t top_k;            /* 1 <= k <= min(n_docs, 4096)                  */
+  int32_t n_docs;
+  int32_t reserved0;
+  int64_t n_pool;           /* = doc_pool_off[n_docs]                       */
+  const void *qr;           /* device [B, Tq, Hr, dr]                       */
+  const void *kr_pooled;    /* device [n_pool, Hr, dr]                      */
+  const int64_t *doc_pool_off; /* device [n_docs+1]; every doc >= 1 row     */
+  float *doc_scores;        /* device out [B, n_docs]                       */
+  int32_t *topk_idx;        /* device out [B, k]                            */
+  float *topk_score;        /* device out [B, k]                            */
+  void *workspace;          /* device, msa_route_workspace_bytes() bytes    */
+  size_t workspace_bytes;
+  /* context assembly; all NULL / 0 to skip */
+  const void *host_kv;              /* pinned host [n_pool, 2, Hkv, D]      */
+  const int64_t *host_doc_pool_off; /* host [n_docs+1], same as device copy */
+  int32_t kv_dtype;                 /* msa_dtype of host_kv and mem_kv      */
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t mem_cap;                  /* rows per query in mem_kv             */
+  int32_t append;                   /* 1: append after host_mem_len[b]      */
+  int32_t reserved1;
+  void *mem_kv;                     /* device [B, mem_cap, 2, Hkv, D]       */
+  int32_t *mem_len;                 /* device out [B]                       */
+  int32_t *host_topk_idx;           /* pinned host out [B, k]               */
+  int32_t *host_mem_len;            /* pinned host in/out [B]               */
+  int32_t *host_mem_docs;           /* pinned host out [B] docs taken; opt. */
+  void *copy_stream;                /* hipStream_t for the copies           */
+  /* profiling, optional: hipEvent_t values recorded on `stream` right before
+   * and right after the bank-scan kernel; NULL to skip */
+  void *prof_event_begin;
+  void *prof_event_end;
+} msa_route_args;
+
+int msa_route(const msa_route_args *args, void *stream);
+
+/* Workspace for msa_route, in bytes (0 on invalid sizes). */
+size_t msa_route_workspace_bytes(int32_t dtype, int32_t batch, int32_t q_tokens,
+                                 int32_t n_router_heads, int32_t router_dim,
+                                 int32_t n_docs, int64_t n_pool, int32_t top_k);
+
+/* ------------------------------------------------------------------------
+ * Stage 3 - one sparse decode-attention step.
+ *
+ * For query b with o = pos_offset[b], T = local_len[b], M = mem_len[b]:
+ *   q'   = RoPE(q[b,h], o + T - 1)
+ *   keys = [ K_bar rows mem_kv[b, 0..M, 0]  (used as stored: already
+ *            rotated per document by msa_pool_encode) ;
+ *            RoPE(local_k[b,i], o + i) for i < T ]
+ *   vals = [ mem_kv[b, 0..M, 1] ; local_v[b, 0..T] ]
+ *   out[b,h] = softmax(scale * keys[:, g] . q') . vals[:, g],
+ *   g = h / (Hq/Hkv),  lse[b,h] = logsumexp of the logits.
+ * The offset o is the number of retrieved documents k in the method's
+ * global RoPE (order: background, then query, then generation), same
+ * sources as above.  A query with no keys gets out = 0, lse = -inf.
+ * M and T are clamped to [0, mem_cap] and [0, local_cap].  fp32 softmax and
+ * accumulation; out is rounded to nearest-even into `dtype`.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;            /* msa_dtype of q, mem_kv, local_k/v, out       */
+  int32_t batch;
+  int32_t n_q_heads;        /* Hq, multiple of Hkv                          */
+  int32_t n_kv_heads;       /* Hkv                                          */
+  int32_t head_dim;         /* D in {64, 128}                               */
+  int32_t mem_cap;          /* >= 0                                         */
+  int32_t local_cap;        /* >= 0                                         */
+  int32_t reserved0;
+  const void *q;            /* device [B, Hq, D], before RoPE               */
+  const void *mem_kv;       /* device [B, mem_cap, 2, Hkv, D]; NULL if cap 0 */
+  const int32_t *mem_len;   /* device [B]                                   */
+  const void *local_k;      /* device [B, local_cap, Hkv, D], before RoPE   */
+  const void *local_v;      /* device [B, local_cap, Hkv, D]                */
+  const int32_t *local_len; /* device [B]                                   */
+  const int32_t *pos_offset;/* device [B]                                   */
+  double rope_theta;        /* > 0                                          */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(D)                       */
+  int32_t reserved1;
+  void *out;                /* device out [B, Hq, D]                        */
+  float *lse;               /* device out [B, Hq]; may be NULL              */
+  void *workspace;          /* device, msa_decode_workspace_bytes() bytes   */
+  size_t workspace_bytes;
+  /* profiling, optional: hipEvent_t values recorded on `stream` right before
+   * and right after the split-KV attention kernel; NULL to skip */
+  void *prof_event_begin;
+  void *prof_event_end;
+} msa_decode_args;
+
+int msa_sparse_decode(const msa_decode_args *args, void *stream);
+
+/* Workspace for msa_sparse_decode, in bytes (0 on invalid sizes). */
+size_t msa_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
+                                  int32_t mem_cap, int32_t local_cap);
+
+/* Thread-local description of the last non-OK return on this thread. */
+const char *msa_last_error(void);
+
+/* Library version, MAJOR * 10000 + MINOR * 100 + PATCH. */
+int msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

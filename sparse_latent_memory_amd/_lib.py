@@ -1,0 +1,257 @@
+"""ctypes binding of libmsa (include/msa.h): argument marshalling only.
+
+Every step of the hot path runs in the HIP library; this module turns torch
+tensors into the C structs of msa.h, allocates outputs the caller did not
+pass (PyTorch is the device-memory and stream provider), and raises
+MSAError on a non-zero status.  If libmsa.so is missing it raises; there is
+no other implementation to fall back to.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_CAPACITY, MSA_ERR_HIP = 0, -1, -2, -3, -4, -5
+MSA_F32, MSA_BF16 = 0, 1
+
+_DTYPE = {torch.float32: MSA_F32, torch.bfloat16: MSA_BF16}
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+I64 = ctypes.c_int64
+
+
+class MSAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"libmsa status {status}: {message}")
+        self.status = status
+
+
+class PoolArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", I32), ("n_docs", I32), ("n_tokens", I64), ("n_pool", I64),
+        ("pool_size", I32), ("n_kv_heads", I32), ("head_dim", I32), ("n_router_heads", I32),
+        ("router_dim", I32), ("reserved0", I32), ("rope_theta", ctypes.c_double),
+        ("doc_tok_off", P), ("doc_pool_off", P), ("k", P), ("v", P), ("kr", P),
+        ("kv_pooled", P), ("kr_pooled", P),
+    ]
+
+
+class RouteArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", I32), ("batch", I32), ("q_tokens", I32), ("n_router_heads", I32),
+        ("router_dim", I32), ("top_k", I32), ("n_docs", I32), ("reserved0", I32), ("n_pool", I64),
+        ("qr", P), ("kr_pooled", P), ("doc_pool_off", P), ("doc_scores", P), ("topk_idx", P),
+        ("topk_score", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
+        ("host_kv", P), ("host_doc_pool_off", P), ("kv_dtype", I32), ("n_kv_heads", I32), ("head_dim", I32),
+        ("mem_cap", I32), ("append", I32), ("reserved1", I32), ("mem_kv", P), ("mem_len", P), ("host_topk_idx", P),
+        ("host_mem_len", P), ("host_mem_docs", P), ("copy_stream", P),
+        ("prof_event_begin", P), ("prof_event_end", P),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", I32), ("batch", I32), ("n_q_heads", I32), ("n_kv_heads", I32), ("head_dim", I32),
+        ("mem_cap", I32), ("local_cap", I32), ("reserved0", I32),
+        ("q", P), ("mem_kv", P), ("mem_len", P), ("local_k", P), ("local_v", P), ("local_len", P),
+        ("pos_offset", P), ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+        ("reserved1", I32), ("out", P), ("lse", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
+        ("prof_event_begin", P), ("prof_event_end", P),
+    ]
+
+
+EXPORTS = ("msa_pool_encode", "msa_route", "msa_route_workspace_bytes", "msa_sparse_decode",
+           "msa_decode_workspace_bytes", "msa_last_error", "msa_version")
+
+_lib = None
+
+
+def load(path=None):
+    """Load libmsa.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libmsa.so is not built ({p}); run `python -m sparse_latent_memory_amd.build` "
+                           "or __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    lib.msa_pool_encode.argtypes = [ctypes.POINTER(PoolArgs), P]
+    lib.msa_pool_encode.restype = ctypes.c_int
+    lib.msa_route.argtypes = [ctypes.POINTER(RouteArgs), P]
+    lib.msa_route.restype = ctypes.c_int
+    lib.msa_sparse_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
+    lib.msa_sparse_decode.restype = ctypes.c_int
+    lib.msa_route_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I64, I32]
+    lib.msa_route_workspace_bytes.restype = ctypes.c_size_t
+    lib.msa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.msa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.msa_last_error.argtypes = []
+    lib.msa_last_error.restype = ctypes.c_char_p
+    lib.msa_version.argtypes = []
+    lib.msa_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != MSA_OK:
+        raise MSAError(status, load().msa_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dtype_code(dtype):
+    try:
+        return _DTYPE[dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {dtype}; libmsa takes float32 or bfloat16") from None
+
+
+# --------------------------------------------------------------------------
+# stage 1
+# --------------------------------------------------------------------------
+
+def pool_encode(k, v, kr, doc_tok_off, doc_pool_off, pool_size, rope_theta, n_pool,
+                kv_pooled=None, kr_pooled=None, stream=None):
+    """msa_pool_encode.  k, v: [T, Hkv, D]; kr: [T, Hr, dr] (device, same
+    dtype); offsets: int64 device [n_docs+1].  Returns (kv_pooled, kr_pooled)."""
+    n_tok, hkv, d = k.shape
+    _, hr, dr = kr.shape
+    if kv_pooled is None:
+        kv_pooled = torch.empty((n_pool, 2, hkv, d), dtype=k.dtype, device=k.device)
+    if kr_pooled is None:
+        kr_pooled = torch.empty((n_pool, hr, dr), dtype=k.dtype, device=k.device)
+    a = PoolArgs(dtype=dtype_code(k.dtype), n_docs=doc_tok_off.numel() - 1, n_tokens=n_tok, n_pool=n_pool,
+                 pool_size=pool_size, n_kv_heads=hkv, head_dim=d, n_router_heads=hr, router_dim=dr,
+                 rope_theta=float(rope_theta), doc_tok_off=_ptr(doc_tok_off), doc_pool_off=_ptr(doc_pool_off),
+                 k=_ptr(k), v=_ptr(v), kr=_ptr(kr), kv_pooled=_ptr(kv_pooled), kr_pooled=_ptr(kr_pooled))
+    _check(load().msa_pool_encode(ctypes.byref(a), _stream(stream)))
+    return kv_pooled, kr_pooled
+
+
+# --------------------------------------------------------------------------
+# stage 2
+# --------------------------------------------------------------------------
+
+def route_workspace_bytes(dtype, batch, q_tokens, n_router_heads, router_dim, n_docs, n_pool, top_k):
+    return int(load().msa_route_workspace_bytes(dtype_code(dtype), batch, q_tokens, n_router_heads,
+                                                router_dim, n_docs, n_pool, top_k))
+
+
+class Assembly:
+    """Buffers of the optional context-assembly part of msa_route."""
+
+    def __init__(self, host_kv, host_doc_pool_off, mem_kv, mem_len, host_topk_idx, host_mem_len,
+                 host_mem_docs=None, append=False, copy_stream=None):
+        self.host_kv = host_kv
+        self.host_doc_pool_off = host_doc_pool_off
+        self.mem_kv = mem_kv
+        self.mem_len = mem_len
+        self.host_topk_idx = host_topk_idx
+        self.host_mem_len = host_mem_len
+        self.host_mem_docs = host_mem_docs
+        self.append = append
+        self.copy_stream = copy_stream
+
+    @classmethod
+    def allocate(cls, host_kv, host_doc_pool_off, batch, top_k, mem_cap, device, copy_stream=None):
+        _, two, hkv, d = host_kv.shape
+        mem_kv = torch.zeros((batch, mem_cap, two, hkv, d), dtype=host_kv.dtype, device=device)
+        return cls(host_kv, host_doc_pool_off, mem_kv, torch.zeros(batch, dtype=torch.int32, device=device),
+                   torch.zeros((batch, top_k), dtype=torch.int32, pin_memory=True),
+                   torch.zeros(batch, dtype=torch.int32, pin_memory=True),
+                   torch.zeros(batch, dtype=torch.int32, pin_memory=True), copy_stream=copy_stream)
+
+
+def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, topk_score=None,
+          workspace=None, assembly=None, stream=None, prof_events=None):
+    """msa_route.  qr: [B, Tq, Hr, dr]; kr_pooled: [n_pool, Hr, dr];
+    doc_pool_off: int64 device [n_docs+1].  Returns (topk_idx, topk_score,
+    doc_scores)."""
+    b, tq, hr, dr = qr.shape
+    n_pool = kr_pooled.shape[0]
+    n_docs = doc_pool_off.numel() - 1
+    dev = qr.device
+    if doc_scores is None:
+        doc_scores = torch.empty((b, n_docs), dtype=torch.float32, device=dev)
+    if topk_idx is None:
+        topk_idx = torch.empty((b, top_k), dtype=torch.int32, device=dev)
+    if topk_score is None:
+        topk_score = torch.empty((b, top_k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = route_workspace_bytes(qr.dtype, b, tq, hr, dr, n_docs, n_pool, top_k)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    a = RouteArgs(dtype=dtype_code(qr.dtype), batch=b, q_tokens=tq, n_router_heads=hr, router_dim=dr,
+                  top_k=top_k, n_docs=n_docs, n_pool=n_pool, qr=_ptr(qr), kr_pooled=_ptr(kr_pooled),
+                  doc_pool_off=_ptr(doc_pool_off), doc_scores=_ptr(doc_scores), topk_idx=_ptr(topk_idx),
+                  topk_score=_ptr(topk_score), workspace=_ptr(workspace), workspace_bytes=workspace.numel())
+    if assembly is not None:
+        asm = assembly
+        a.host_kv = _ptr(asm.host_kv)
+        a.host_doc_pool_off = _ptr(asm.host_doc_pool_off)
+        a.kv_dtype = dtype_code(asm.host_kv.dtype)
+        a.n_kv_heads = asm.host_kv.shape[2]
+        a.head_dim = asm.host_kv.shape[3]
+        a.mem_cap = asm.mem_kv.shape[1]
+        a.append = 1 if asm.append else 0
+        a.mem_kv = _ptr(asm.mem_kv)
+        a.mem_len = _ptr(asm.mem_len)
+        a.host_topk_idx = _ptr(asm.host_topk_idx)
+        a.host_mem_len = _ptr(asm.host_mem_len)
+        a.host_mem_docs = _ptr(asm.host_mem_docs)
+        cs = asm.copy_stream if asm.copy_stream is not None else stream
+        a.copy_stream = _stream(cs)
+    if prof_events is not None:
+        a.prof_event_begin, a.prof_event_end = prof_events
+    _check(load().msa_route(ctypes.byref(a), _stream(stream)))
+    return topk_idx, topk_score, doc_scores
+
+
+# --------------------------------------------------------------------------
+# stage 3
+# --------------------------------------------------------------------------
+
+def decode_workspace_bytes(batch, n_q_heads, head_dim, mem_cap, local_cap):
+    return int(load().msa_decode_workspace_bytes(batch, n_q_heads, head_dim, mem_cap, local_cap))
+
+
+def sparse_decode(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, rope_theta,
+                  out=None, lse=None, workspace=None, softmax_scale=0.0, want_lse=True, stream=None,
+                  prof_events=None):
+    """msa_sparse_decode.  q: [B, Hq, D]; mem_kv: [B, M_cap, 2, Hkv, D] (or
+    None); local_k/v: [B, T_cap, Hkv, D]; mem_len, local_len, pos_offset:
+    int32 device [B].  Returns (out, lse)."""
+    b, hq, d = q.shape
+    _, t_cap, hkv, _ = local_k.shape
+    m_cap = 0 if mem_kv is None else mem_kv.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = decode_workspace_bytes(b, hq, d, m_cap, t_cap)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    a = DecodeArgs(dtype=dtype_code(q.dtype), batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, mem_cap=m_cap,
+                   local_cap=t_cap, q=_ptr(q), mem_kv=_ptr(mem_kv), mem_len=_ptr(mem_len), local_k=_ptr(local_k),
+                   local_v=_ptr(local_v), local_len=_ptr(local_len), pos_offset=_ptr(pos_offset),
+                   rope_theta=float(rope_theta), softmax_scale=float(softmax_scale), out=_ptr(out),
+                   lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=workspace.numel())
+    if prof_events is not None:
+        a.prof_event_begin, a.prof_event_end = prof_events
+    _check(load().msa_sparse_decode(ctypes.byref(a), _stream(stream)))
+    return out, lse

@@ -1,0 +1,296 @@
+// Stage 3: one sparse decode-attention step over [pooled memory ; local K/V].
+//
+// Method: "EverMind-AI/MSA: Memory Sparse Attention for 100M-Token Contexts"
+// (hysenlabs.com), section "How MSA compresses and routes documents" (the
+// selected documents' compressed K/V are concatenated with the query's local
+// K/V; global RoPE offsets the query start by k, order background -> query ->
+// generation) and stage 3 of "EverMind Releases Memory-Sparse Attention Code
+// for Long-Context AI Models" (toolmesh.ai), "Architectural Design and
+// Inference".
+//
+// Split-KV design: grid (split, kv head, query).  Each workgroup owns a
+// contiguous key range of one (query, KV head) and all Hq/Hkv query heads of
+// that group (they share every staged K/V tile).  Per 64-key tile:
+//   stage   K (local keys rotated at o + i on the way into LDS; memory keys are
+//           used as stored) and V into LDS as fp32, coalesced 16-byte loads;
+//   scores  wave w <-> query head, lane <-> key: dot(q', K[key]) from LDS;
+//   softmax online, wave-wide max/sum, exp2 with log2(e) folded into q';
+//   PV      wave w <-> query head, lane <-> D/64 output dims.
+// Partials (m, l, unnormalised acc) go to the workspace; a merge kernel
+// combines the splits with their log-sum-exp weights.
+#include "msa_internal.h"
+
+#include <algorithm>
+
+namespace msa {
+namespace {
+
+constexpr int kTile = 64;
+constexpr int kMaxGroup = 8;   // query heads per KV head handled per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const T *__restrict__ q, const T *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
+    const T *__restrict__ local_k, const T *__restrict__ local_v, const int32_t *__restrict__ local_len,
+    const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc, float *__restrict__ part_ml,
+    int Hq, int Hkv, int mem_cap, int local_cap, int split_len, int n_split, float scale_log2,
+    double log2_theta) {
+  constexpr int VW = Elt<T>::kPerVec;
+  constexpr int HALF = D / 2;
+  constexpr int KSTR = D + 4;             // padded LDS row (conflict-free row reads)
+  constexpr int DPL = D / 64;             // output dims per lane
+  __shared__ __align__(16) float ks[kTile * KSTR];
+  __shared__ __align__(16) float vs[kTile * D];
+  __shared__ __align__(16) float qs[kMaxGroup * D];
+  __shared__ float ps[kMaxGroup * kTile];
+  __shared__ double omega[HALF];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int M = max(0, min(mem_len[b], mem_cap));
+  const int Tl = max(0, min(local_len[b], local_cap));
+  const int o = pos_offset[b];
+  const int total = M + Tl;
+  const int k0 = split * split_len;
+  const int k1 = min(total, k0 + split_len);
+
+  // output slots of this (query, split) for the G heads of the group
+  auto slot = [&](int hh) { return ((int64_t)b * Hq + g * G + hh) * n_split + split; };
+
+  if (k0 >= k1) {
+    for (int hh = threadIdx.x; hh < G; hh += blockDim.x) {
+      part_ml[2 * slot(hh)] = -INFINITY;
+      part_ml[2 * slot(hh) + 1] = 0.f;
+    }
+    return;
+  }
+
+  for (int j = threadIdx.x; j < HALF; j += blockDim.x) omega[j] = exp2(-(2.0 * j / D) * log2_theta);
+  __syncthreads();
+  // q' = RoPE(q, o + Tl - 1), with the softmax scale and log2(e) folded in
+  for (int t = threadIdx.x; t < G * HALF; t += blockDim.x) {
+    const int hh = t / HALF, j = t % HALF;
+    const T *src = q + ((int64_t)b * Hq + g * G + hh) * D;
+    const float x1 = Elt<T>::get(src, j), x2 = Elt<T>::get(src, j + HALF);
+    float c, s;
+    rope_phasor((double)o + (double)Tl - 1.0, omega[j], &c, &s);
+    qs[hh * D + j] = (x1 * c - x2 * s) * scale_log2;
+    qs[hh * D + j + HALF] = (x2 * c + x1 * s) * scale_log2;
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float acc[2][DPL];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[r][i] = 0.f;
+
+  const int64_t mem_row = 2LL * Hkv * D;      // elements per pooled memory row
+  const int64_t loc_row = (int64_t)Hkv * D;   // elements per local token
+
+  for (int kt = k0; kt < k1; kt += kTile) {
+    const int nk = min(kTile, k1 - kt);
+    __syncthreads();  // previous tile fully consumed (and qs written on the first pass)
+    // ---- stage K (rotated when local) ----
+    constexpr int KCH = HALF / VW;   // 16-byte pair-chunks per key
+    for (int task = threadIdx.x; task < kTile * KCH; task += blockDim.x) {
+      const int kk = task / KCH, cj = (task % KCH) * VW;
+      float xl[VW], xh[VW];
+      if (kk < nk) {
+        const int key = kt + kk;
+        if (key < M) {
+          const T *src = mem_kv + ((int64_t)b * mem_cap + key) * mem_row + (int64_t)g * D;
+          Elt<T>::unpack(ld16(src + cj), xl);
+          Elt<T>::unpack(ld16(src + cj + HALF), xh);
+        } else {
+          const int i = key - M;
+          const T *src = local_k + ((int64_t)b * local_cap + i) * loc_row + (int64_t)g * D;
+          float rl[VW], rh[VW];
+          Elt<T>::unpack(ld16(src + cj), rl);
+          Elt<T>::unpack(ld16(src + cj + HALF), rh);
+#pragma unroll
+          for (int e = 0; e < VW; ++e) {
+            float c, s;
+            rope_phasor((double)o + (double)i, omega[cj + e], &c, &s);
+            xl[e] = rl[e] * c - rh[e] * s;
+            xh[e] = rh[e] * c + rl[e] * s;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) xl[e] = xh[e] = 0.f;
+      }
+      float *dst = ks + kk * KSTR + cj;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) { dst[e] = xl[e]; dst[e + HALF] = xh[e]; }
+    }
+    // ---- stage V ----
+    constexpr int VCH = D / VW;
+    for (int task = threadIdx.x; task < kTile * VCH; task += blockDim.x) {
+      const int kk = task / VCH, cj = (task % VCH) * VW;
+      float x[VW];
+      if (kk < nk) {
+        const int key = kt + kk;
+        const T *src = key < M ? mem_kv + ((int64_t)b * mem_cap + key) * mem_row + loc_row + (int64_t)g * D
+                               : local_v + ((int64_t)b * local_cap + (key - M)) * loc_row + (int64_t)g * D;
+        Elt<T>::unpack(ld16(src + cj), x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VW; ++e) x[e] = 0.f;
+      }
+      float *dst = vs + kk * D + cj;
+#pragma unroll
+      for (int e = 0; e < VW; ++e) dst[e] = x[e];
+    }
+    __syncthreads();
+
+    // ---- scores, online softmax, PV: wave <-> query head ----
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int hh = wave + 4 * r;
+      if (hh >= G) break;
+      float logit = -INFINITY;
+      if (lane < nk) {
+        const float *kr = ks + lane * KSTR;
+        const float *qr = qs + hh * D;
+        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+#pragma unroll
+        for (int i = 0; i < D; i += 4) {
+          acc0 += qr[i] * kr[i];
+          acc1 += qr[i + 1] * kr[i + 1];
+          acc2 += qr[i + 2] * kr[i + 2];
+          acc3 += qr[i + 3] * kr[i + 3];
+        }
+        logit = (acc0 + acc1) + (acc2 + acc3);
+      }
+      const float m_tile = wave_max(logit);
+      const float m_new = fmaxf(m_run[r], m_tile);
+      const float p = lane < nk ? exp2f(logit - m_new) : 0.f;
+      const float corr = exp2f(m_run[r] - m_new);   // 0 on the first tile (m_run = -inf)
+      l_run[r] = l_run[r] * corr + wave_sum(p);
+      m_run[r] = m_new;
+      ps[hh * kTile + lane] = p;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[r][i] *= corr;
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      const float *pr = ps + hh * kTile;
+      for (int kk = 0; kk < nk; ++kk) {
+        const float w = pr[kk];
+        const float *vr = vs + kk * D + lane * DPL;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[r][i] += w * vr[i];
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int hh = wave + 4 * r;
+    if (hh >= G) break;
+    const int64_t sl = slot(hh);
+    float *dst = part_acc + sl * D + lane * DPL;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) dst[i] = acc[r][i];
+    if (lane == 0) {
+      part_ml[2 * sl] = m_run[r];
+      part_ml[2 * sl + 1] = l_run[r];
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float *__restrict__ part_acc,
+                                                        const float *__restrict__ part_ml, T *__restrict__ out,
+                                                        float *__restrict__ lse, int n_split) {
+  const int64_t bh = blockIdx.x;
+  const float *ml = part_ml + bh * n_split * 2;
+  float m = -INFINITY;
+  for (int s = 0; s < n_split; ++s) m = fmaxf(m, ml[2 * s]);
+  float L = 0.f, acc = 0.f;
+  if (m > -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float ms = ml[2 * s];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - m);
+      L += w * ml[2 * s + 1];
+      acc += w * part_acc[(bh * n_split + s) * D + threadIdx.x];
+    }
+  }
+  const float o = L > 0.f ? acc / L : 0.f;
+  Elt<T>::put(out, bh * D + threadIdx.x, o);
+  if (lse && threadIdx.x == 0) lse[bh] = L > 0.f ? (m + log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+int choose_split_len(int32_t batch, int32_t mem_cap, int32_t local_cap) {
+  const int64_t total = (int64_t)mem_cap + local_cap;
+  int64_t len = (total * batch + 255) / 256;
+  len = ((len + kTile - 1) / kTile) * kTile;
+  if (len < kTile) len = kTile;
+  return (int)len;
+}
+
+template <typename T, int D>
+hipError_t launch_t(const msa_decode_args &a, float *part_acc, float *part_ml, int32_t n_split, hipStream_t s) {
+  const int split_len = choose_split_len(a.batch, a.mem_cap, a.local_cap);
+  const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.0f / sqrtf((float)a.head_dim);
+  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a.prof_event_begin);
+  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a.prof_event_end);
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(n_split, a.n_kv_heads, a.batch), dim3(256), 0, s,
+                     reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.mem_kv), a.mem_len,
+                     reinterpret_cast<const T *>(a.local_k), reinterpret_cast<const T *>(a.local_v),
+                     a.local_len, a.pos_offset, part_acc, part_ml, a.n_q_heads, a.n_kv_heads, a.mem_cap,
+                     a.local_cap, split_len, n_split, scale * kLog2e, log2(a.rope_theta));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.batch * a.n_q_heads), dim3(D), 0, s, part_acc,
+                     part_ml, reinterpret_cast<T *>(a.out), a.lse, n_split);
+  return hipGetLastError();
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t decode_ws_layout(int32_t batch, int32_t hq, int32_t d, int32_t mem_cap, int32_t local_cap, void *base,
+                        float **part_acc, float **part_ml, int32_t *n_split) {
+  const int split_len = choose_split_len(batch, mem_cap, local_cap);
+  const int64_t total = (int64_t)mem_cap + local_cap;
+  const int32_t ns = (int32_t)std::max<int64_t>(1, (total + split_len - 1) / split_len);
+  const size_t slots = (size_t)batch * hq * ns;
+  const size_t o_acc = 0;
+  const size_t o_ml = align256(sizeof(float) * slots * d);
+  const size_t end = align256(o_ml + sizeof(float) * 2 * slots);
+  if (base) {
+    *part_acc = reinterpret_cast<float *>(reinterpret_cast<char *>(base) + o_acc);
+    *part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(base) + o_ml);
+  }
+  if (n_split) *n_split = ns;
+  return end;
+}
+
+hipError_t launch_decode(const msa_decode_args &a, float *part_acc, float *part_ml, int32_t n_split,
+                         hipStream_t s) {
+  if (a.dtype == MSA_BF16)
+    return a.head_dim == 128 ? launch_t<uint16_t, 128>(a, part_acc, part_ml, n_split, s)
+                             : launch_t<uint16_t, 64>(a, part_acc, part_ml, n_split, s);
+  return a.head_dim == 128 ? launch_t<float, 128>(a, part_acc, part_ml, n_split, s)
+                           : launch_t<float, 64>(a, part_acc, part_ml, n_split, s);
+}
+
+}  // namespace msa

@@ -1,0 +1,253 @@
+// C ABI entry points of libmsa: argument checks, workspace carving, the
+// host-driven context assembly, and error reporting.  Kernels live in
+// pool.hip, route.hip and decode.hip.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
+#include "msa_internal.h"
+
+namespace msa {
+
+bool route_shape_supported(int32_t hr, int32_t dr);
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(MSA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int32_t d) { return d == MSA_F32 || d == MSA_BF16; }
+size_t elt_size(int32_t d) { return d == MSA_BF16 ? 2 : 4; }
+bool dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+// per-thread, per-device events for the assembly path
+struct ThreadEvents {
+  int device = -1;
+  hipEvent_t topk = nullptr, copies = nullptr;
+  ~ThreadEvents() {
+    if (topk) (void)hipEventDestroy(topk);
+    if (copies) (void)hipEventDestroy(copies);
+  }
+};
+thread_local ThreadEvents g_ev;
+
+hipError_t thread_events(ThreadEvents **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (g_ev.device != dev) {
+    if (g_ev.topk) (void)hipEventDestroy(g_ev.topk);
+    if (g_ev.copies) (void)hipEventDestroy(g_ev.copies);
+    g_ev.topk = g_ev.copies = nullptr;
+    if ((e = hipEventCreateWithFlags(&g_ev.topk, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&g_ev.copies, hipEventDisableTiming)) != hipSuccess) return e;
+    g_ev.device = dev;
+  }
+  *out = &g_ev;
+  return hipSuccess;
+}
+
+}  // namespace
+
+const DeviceInfo &device_info() {
+  static DeviceInfo info[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::call_once(once[dev], [dev] {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess && p.multiProcessorCount > 0)
+      info[dev].n_cu = p.multiProcessorCount;
+  });
+  return info[dev];
+}
+
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+const char *msa_last_error(void) { return g_err; }
+
+int msa_version(void) { return 100; }
+
+int msa_pool_encode(const msa_pool_args *a, void *stream) {
+  if (!a) return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: args is NULL");
+  if (!dtype_ok(a->dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: bad dtype %d", a->dtype);
+  if (a->n_docs < 1 || a->n_tokens < a->n_docs || a->n_pool < a->n_docs || a->pool_size < 1 ||
+      a->n_kv_heads < 1 || a->n_router_heads < 1 || !(a->rope_theta > 0.0))
+    return fail(MSA_ERR_INVALID_ARG,
+                "msa_pool_encode: need n_docs >= 1, n_tokens >= n_docs, n_pool >= n_docs, pool_size >= 1, "
+                "heads >= 1, rope_theta > 0");
+  if (a->n_pool > a->n_tokens)
+    return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: n_pool (%lld) exceeds n_tokens (%lld)",
+                (long long)a->n_pool, (long long)a->n_tokens);
+  if (!dim_ok(a->head_dim) || !dim_ok(a->router_dim))
+    return fail(MSA_ERR_UNSUPPORTED, "msa_pool_encode: head_dim and router_dim must be 64 or 128");
+  const int vw = a->dtype == MSA_BF16 ? 8 : 4;
+  const int tasks = a->n_kv_heads * a->head_dim / 2 / vw + a->n_kv_heads * a->head_dim / vw +
+                    a->n_router_heads * a->router_dim / vw;
+  if (tasks > 4096) return fail(MSA_ERR_UNSUPPORTED, "msa_pool_encode: too many heads (%d vector tasks)", tasks);
+  if (!a->doc_tok_off || !a->doc_pool_off || !a->k || !a->v || !a->kr || !a->kv_pooled || !a->kr_pooled)
+    return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: NULL pointer");
+  if (!aligned16(a->k) || !aligned16(a->v) || !aligned16(a->kr) || !aligned16(a->kv_pooled) ||
+      !aligned16(a->kr_pooled))
+    return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: tensors must be 16-byte aligned");
+  hipError_t e = launch_pool(*a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_pool_encode launch");
+}
+
+size_t msa_route_workspace_bytes(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t n_router_heads,
+                                 int32_t router_dim, int32_t n_docs, int64_t n_pool, int32_t top_k) {
+  if (!dtype_ok(dtype) || batch < 1 || q_tokens < 1 || n_router_heads < 1 || router_dim < 1 || n_docs < 1 ||
+      n_pool < n_docs || top_k < 1)
+    return 0;
+  return route_ws_layout(dtype, batch, q_tokens, n_router_heads, router_dim, n_docs, n_pool, top_k, nullptr,
+                         nullptr);
+}
+
+int msa_route(const msa_route_args *a, void *stream) {
+  if (!a) return fail(MSA_ERR_INVALID_ARG, "msa_route: args is NULL");
+  if (!dtype_ok(a->dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_route: bad dtype %d", a->dtype);
+  if (a->batch < 1 || a->q_tokens < 1 || a->n_docs < 1 || a->n_pool < a->n_docs)
+    return fail(MSA_ERR_INVALID_ARG, "msa_route: need batch, q_tokens, n_docs >= 1 and n_pool >= n_docs");
+  if (a->n_docs > 0x7ffffffe) return fail(MSA_ERR_UNSUPPORTED, "msa_route: too many documents");
+  if (a->top_k < 1 || a->top_k > a->n_docs)
+    return fail(MSA_ERR_INVALID_ARG, "msa_route: need 1 <= top_k (%d) <= n_docs (%d)", a->top_k, a->n_docs);
+  if (a->top_k > kMaxTopK) return fail(MSA_ERR_UNSUPPORTED, "msa_route: top_k > %d", kMaxTopK);
+  if (!route_shape_supported(a->n_router_heads, a->router_dim))
+    return fail(MSA_ERR_UNSUPPORTED,
+                "msa_route: router_dim must be 64 or 128 and n_router_heads a power of two dividing 64 with "
+                "n_router_heads * router_dim <= 2048");
+  if (!a->qr || !a->kr_pooled || !a->doc_pool_off || !a->doc_scores || !a->topk_idx || !a->topk_score)
+    return fail(MSA_ERR_INVALID_ARG, "msa_route: NULL pointer");
+  if (!aligned16(a->qr) || !aligned16(a->kr_pooled))
+    return fail(MSA_ERR_INVALID_ARG, "msa_route: qr and kr_pooled must be 16-byte aligned");
+  const size_t need = route_ws_layout(a->dtype, a->batch, a->q_tokens, a->n_router_heads, a->router_dim,
+                                      a->n_docs, a->n_pool, a->top_k, nullptr, nullptr);
+  if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
+    return fail(MSA_ERR_WORKSPACE, "msa_route: workspace needs %zu bytes (16-byte aligned), got %zu", need,
+                a->workspace ? a->workspace_bytes : (size_t)0);
+  const bool assemble = a->host_kv != nullptr;
+  if (assemble) {
+    if (!a->host_doc_pool_off || !a->mem_kv || !a->mem_len || !a->host_topk_idx || !a->host_mem_len)
+      return fail(MSA_ERR_INVALID_ARG, "msa_route: assembly needs host_doc_pool_off, mem_kv, mem_len, "
+                                       "host_topk_idx and host_mem_len");
+    if (!dtype_ok(a->kv_dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_route: bad kv_dtype %d", a->kv_dtype);
+    if (a->n_kv_heads < 1 || a->head_dim < 1 || a->mem_cap < 0)
+      return fail(MSA_ERR_INVALID_ARG, "msa_route: assembly needs n_kv_heads, head_dim >= 1, mem_cap >= 0");
+    if (a->append) {
+      for (int b = 0; b < a->batch; ++b)
+        if (a->host_mem_len[b] < 0 || a->host_mem_len[b] > a->mem_cap)
+          return fail(MSA_ERR_INVALID_ARG, "msa_route: host_mem_len[%d] = %d outside [0, mem_cap]", b,
+                      a->host_mem_len[b]);
+    }
+  }
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  RouteWs ws;
+  route_ws_layout(a->dtype, a->batch, a->q_tokens, a->n_router_heads, a->router_dim, a->n_docs, a->n_pool,
+                  a->top_k, a->workspace, &ws);
+  hipError_t e = launch_route(*a, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "msa_route launch");
+  if (!assemble) return MSA_OK;
+
+  // ---- context assembly: indices to the host, then one copy per document ----
+  ThreadEvents *ev = nullptr;
+  if ((e = thread_events(&ev)) != hipSuccess) return hip_fail(e, "msa_route events");
+  const size_t idx_bytes = sizeof(int32_t) * (size_t)a->batch * a->top_k;
+  if ((e = hipMemcpyAsync(a->host_topk_idx, a->topk_idx, idx_bytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return hip_fail(e, "msa_route top-k to host");
+  if ((e = hipEventRecord(ev->topk, s)) != hipSuccess) return hip_fail(e, "msa_route event record");
+  if ((e = hipEventSynchronize(ev->topk)) != hipSuccess) return hip_fail(e, "msa_route wait for top-k");
+
+  hipStream_t cs = reinterpret_cast<hipStream_t>(a->copy_stream);
+  const size_t row_bytes = 2 * (size_t)a->n_kv_heads * a->head_dim * elt_size(a->kv_dtype);
+  const char *src = reinterpret_cast<const char *>(a->host_kv);
+  char *dst = reinterpret_cast<char *>(a->mem_kv);
+  const int64_t *off = a->host_doc_pool_off;
+  for (int b = 0; b < a->batch; ++b) {
+    int64_t len = a->append ? a->host_mem_len[b] : 0;
+    int taken = 0;
+    for (int r = 0; r < a->top_k; ++r) {
+      const int32_t d = a->host_topk_idx[(size_t)b * a->top_k + r];
+      if (d < 0 || d >= a->n_docs) break;
+      const int64_t r0 = off[d], r1 = off[d + 1];
+      if (r0 < 0 || r1 < r0 || r1 > a->n_pool) break;
+      const int64_t rows = r1 - r0;
+      if (len + rows > a->mem_cap) break;
+      if (rows > 0) {
+        e = hipMemcpyAsync(dst + ((size_t)b * a->mem_cap + len) * row_bytes, src + (size_t)r0 * row_bytes,
+                           (size_t)rows * row_bytes, hipMemcpyHostToDevice, cs);
+        if (e != hipSuccess) return hip_fail(e, "msa_route gather copy");
+      }
+      len += rows;
+      ++taken;
+    }
+    a->host_mem_len[b] = (int32_t)len;
+    if (a->host_mem_docs) a->host_mem_docs[b] = taken;
+  }
+  if ((e = hipMemcpyAsync(a->mem_len, a->host_mem_len, sizeof(int32_t) * a->batch, hipMemcpyHostToDevice, cs)) !=
+      hipSuccess)
+    return hip_fail(e, "msa_route mem_len copy");
+  if ((e = hipEventRecord(ev->copies, cs)) != hipSuccess) return hip_fail(e, "msa_route event record");
+  if ((e = hipStreamWaitEvent(s, ev->copies, 0)) != hipSuccess) return hip_fail(e, "msa_route stream wait");
+  return MSA_OK;
+}
+
+size_t msa_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim, int32_t mem_cap,
+                                  int32_t local_cap) {
+  if (batch < 1 || n_q_heads < 1 || !dim_ok(head_dim) || mem_cap < 0 || local_cap < 0) return 0;
+  return decode_ws_layout(batch, n_q_heads, head_dim, mem_cap, local_cap, nullptr, nullptr, nullptr, nullptr);
+}
+
+int msa_sparse_decode(const msa_decode_args *a, void *stream) {
+  if (!a) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: args is NULL");
+  if (!dtype_ok(a->dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: bad dtype %d", a->dtype);
+  if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1 || a->mem_cap < 0 || a->local_cap < 0 ||
+      !(a->rope_theta > 0.0))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: need batch, heads >= 1, caps >= 0, rope_theta > 0");
+  if (a->n_q_heads % a->n_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: n_q_heads (%d) not a multiple of n_kv_heads (%d)",
+                a->n_q_heads, a->n_kv_heads);
+  if (a->n_q_heads / a->n_kv_heads > 8)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_decode: more than 8 query heads per KV head");
+  if (!dim_ok(a->head_dim)) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_decode: head_dim must be 64 or 128");
+  if ((int64_t)a->mem_cap + a->local_cap > (1LL << 30))
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_decode: context capacity too large");
+  if (!a->q || !a->mem_len || !a->local_len || !a->pos_offset || !a->out || (a->mem_cap > 0 && !a->mem_kv) ||
+      (a->local_cap > 0 && (!a->local_k || !a->local_v)))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: NULL pointer");
+  if ((a->mem_kv && !aligned16(a->mem_kv)) || (a->local_k && !aligned16(a->local_k)) ||
+      (a->local_v && !aligned16(a->local_v)))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: K/V tensors must be 16-byte aligned");
+  float *part_acc = nullptr, *part_ml = nullptr;
+  int32_t n_split = 0;
+  const size_t need =
+      decode_ws_layout(a->batch, a->n_q_heads, a->head_dim, a->mem_cap, a->local_cap, nullptr, nullptr, nullptr,
+                       &n_split);
+  if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
+    return fail(MSA_ERR_WORKSPACE, "msa_sparse_decode: workspace needs %zu bytes (16-byte aligned), got %zu",
+                need, a->workspace ? a->workspace_bytes : (size_t)0);
+  decode_ws_layout(a->batch, a->n_q_heads, a->head_dim, a->mem_cap, a->local_cap, a->workspace, &part_acc,
+                   &part_ml, &n_split);
+  hipError_t e = launch_decode(*a, part_acc, part_ml, n_split, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_decode launch");
+}
+
+}  // extern "C"

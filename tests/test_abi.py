@@ -1,0 +1,208 @@
+"""Host-side checks of the C ABI: libmsa.so loads, exports every function
+include/msa.h declares, the ctypes structs have the C layout, and invalid
+arguments are rejected before anything touches a GPU."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime before libmsa)
+
+from sparse_latent_memory_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(msa_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_library_built_and_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+        exported = set(re.findall(r" T (msa_\w+)$", out, re.M))
+        assert set(declared) <= exported
+
+
+def test_version():
+    assert _lib.load().msa_version() == 100
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_ctypes_struct_layout_matches_c(tmp_path):
+    structs = {"msa_pool_args": _lib.PoolArgs, "msa_route_args": _lib.RouteArgs,
+               "msa_decode_args": _lib.DecodeArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("  return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
+
+
+def test_workspace_size_functions():
+    lib = _lib.load()
+    assert lib.msa_route_workspace_bytes(1, 1, 1, 8, 128, 195313, 1562504, 16) >= 4 * 1562504
+    assert lib.msa_route_workspace_bytes(1, 0, 1, 8, 128, 10, 10, 1) == 0          # batch 0
+    assert lib.msa_route_workspace_bytes(7, 1, 1, 8, 128, 10, 10, 1) == 0          # bad dtype
+    assert lib.msa_route_workspace_bytes(1, 1, 1, 8, 128, 10, 9, 1) == 0           # n_pool < n_docs
+    assert lib.msa_decode_workspace_bytes(1, 32, 128, 128, 4096) > 0
+    assert lib.msa_decode_workspace_bytes(1, 32, 96, 128, 4096) == 0               # head_dim 96
+    assert lib.msa_decode_workspace_bytes(1, 32, 128, -1, 4096) == 0
+
+
+# --------------------------------------------------------------------------
+# error paths: every call below must fail validation, before any HIP call.
+# They pass host addresses, so they only run where no GPU is visible.
+# --------------------------------------------------------------------------
+no_gpu = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                            reason="error-path calls pass host pointers; run them without a GPU")
+
+_buf = ctypes.create_string_buffer(1 << 16)
+_B = ctypes.addressof(_buf) + (-ctypes.addressof(_buf) % 256)   # 256-byte aligned host address
+
+
+def _p(off=0):
+    return ctypes.c_void_p(_B + off)
+
+
+def _pool_args(**kw):
+    a = _lib.PoolArgs(dtype=1, n_docs=2, n_tokens=100, n_pool=4, pool_size=64, n_kv_heads=8, head_dim=128,
+                      n_router_heads=8, router_dim=128, rope_theta=1e6, doc_tok_off=_p(), doc_pool_off=_p(),
+                      k=_p(), v=_p(), kr=_p(), kv_pooled=_p(), kr_pooled=_p())
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _call_pool(a):
+    lib = _lib.load()
+    return lib.msa_pool_encode(ctypes.byref(a), None), lib.msa_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", 5, _lib.MSA_ERR_INVALID_ARG),
+    ("n_docs", 0, _lib.MSA_ERR_INVALID_ARG),
+    ("pool_size", 0, _lib.MSA_ERR_INVALID_ARG),
+    ("head_dim", 96, _lib.MSA_ERR_UNSUPPORTED),
+    ("router_dim", 256, _lib.MSA_ERR_UNSUPPORTED),
+    ("rope_theta", 0.0, _lib.MSA_ERR_INVALID_ARG),
+    ("n_pool", 1000, _lib.MSA_ERR_INVALID_ARG),
+    ("k", None, _lib.MSA_ERR_INVALID_ARG),
+    ("kv_pooled", ctypes.c_void_p(_B + 8), _lib.MSA_ERR_INVALID_ARG),   # misaligned
+])
+def test_pool_rejects_bad_arguments(field, value, code):
+    status, msg = _call_pool(_pool_args(**{field: value}))
+    assert status == code, msg
+    assert msg.startswith("msa_pool_encode")
+
+
+@no_gpu
+def test_null_args_rejected():
+    lib = _lib.load()
+    assert lib.msa_pool_encode(None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_route(None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_decode(None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert b"NULL" in lib.msa_last_error()
+
+
+def _route_args(**kw):
+    a = _lib.RouteArgs(dtype=1, batch=1, q_tokens=1, n_router_heads=8, router_dim=128, top_k=4, n_docs=10,
+                       n_pool=20, qr=_p(), kr_pooled=_p(), doc_pool_off=_p(), doc_scores=_p(), topk_idx=_p(),
+                       topk_score=_p(), workspace=_p(), workspace_bytes=16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    ({"top_k": 11}, _lib.MSA_ERR_INVALID_ARG),                  # k > n_docs
+    ({"top_k": 0}, _lib.MSA_ERR_INVALID_ARG),
+    ({"n_docs": 5000, "n_pool": 6000, "top_k": 4097}, _lib.MSA_ERR_UNSUPPORTED),
+    ({"router_dim": 96}, _lib.MSA_ERR_UNSUPPORTED),
+    ({"n_router_heads": 3}, _lib.MSA_ERR_UNSUPPORTED),
+    ({"n_pool": 5}, _lib.MSA_ERR_INVALID_ARG),                  # fewer rows than documents
+    ({"qr": None}, _lib.MSA_ERR_INVALID_ARG),
+    ({}, _lib.MSA_ERR_WORKSPACE),                               # 16 bytes is too small
+    ({"workspace": None}, _lib.MSA_ERR_WORKSPACE),
+])
+def test_route_rejects_bad_arguments(kw, code):
+    lib = _lib.load()
+    a = _route_args(**kw)
+    assert lib.msa_route(ctypes.byref(a), None) == code, lib.msa_last_error()
+
+
+@no_gpu
+def test_route_assembly_arguments_checked_before_launch():
+    lib = _lib.load()
+    need = lib.msa_route_workspace_bytes(1, 1, 1, 8, 128, 10, 20, 4)
+    assert need < len(_buf) - 256
+    a = _route_args(workspace_bytes=need, host_kv=_p())          # assembly without its buffers
+    assert lib.msa_route(ctypes.byref(a), None) == _lib.MSA_ERR_INVALID_ARG
+    assert b"assembly" in lib.msa_last_error()
+    lens = (ctypes.c_int32 * 1)(99)
+    a = _route_args(workspace_bytes=need, host_kv=_p(), host_doc_pool_off=_p(), mem_kv=_p(), mem_len=_p(),
+                    host_topk_idx=_p(), host_mem_len=ctypes.cast(lens, ctypes.c_void_p), kv_dtype=1,
+                    n_kv_heads=8, head_dim=128, mem_cap=10, append=1)
+    assert lib.msa_route(ctypes.byref(a), None) == _lib.MSA_ERR_INVALID_ARG   # 99 > mem_cap
+    assert b"host_mem_len" in lib.msa_last_error()
+    a.kv_dtype = 9
+    assert lib.msa_route(ctypes.byref(a), None) == _lib.MSA_ERR_INVALID_ARG
+    assert b"kv_dtype" in lib.msa_last_error()
+
+
+def _decode_args(**kw):
+    a = _lib.DecodeArgs(dtype=1, batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, mem_cap=128, local_cap=64,
+                        q=_p(), mem_kv=_p(), mem_len=_p(), local_k=_p(), local_v=_p(), local_len=_p(),
+                        pos_offset=_p(), rope_theta=1e6, softmax_scale=0.0, out=_p(), lse=None, workspace=_p(),
+                        workspace_bytes=16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    ({"n_q_heads": 30}, _lib.MSA_ERR_INVALID_ARG),              # not a multiple of Hkv
+    ({"n_q_heads": 72}, _lib.MSA_ERR_UNSUPPORTED),              # 9 query heads per KV head
+    ({"head_dim": 80}, _lib.MSA_ERR_UNSUPPORTED),
+    ({"mem_kv": None}, _lib.MSA_ERR_INVALID_ARG),               # mem_cap > 0 needs memory
+    ({"local_v": None}, _lib.MSA_ERR_INVALID_ARG),
+    ({"rope_theta": -1.0}, _lib.MSA_ERR_INVALID_ARG),
+    ({"local_k": ctypes.c_void_p(_B + 4)}, _lib.MSA_ERR_INVALID_ARG),
+    ({}, _lib.MSA_ERR_WORKSPACE),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    lib = _lib.load()
+    a = _decode_args(**kw)
+    assert lib.msa_sparse_decode(ctypes.byref(a), None) == code, lib.msa_last_error()
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load(str(tmp_path / "missing" / "libmsa.so"))

@@ -1,0 +1,481 @@
+"""GPU parity: every stage of libmsa against the CPU oracle on identical
+seeded inputs, through the C ABI (ctypes binding).  Stage-wise tests feed
+the oracle and the library the same stored inputs; the chain tests run
+pool -> route -> gather -> decode end to end."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_latent_memory_amd as msa
+from parity_util import (TAU, check_decode, check_pool, check_scores, check_topk, check_topk_order, np64,
+                         storage)
+from sparse_latent_memory_amd import _lib, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+THETA = 1e6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    _lib.load()   # raises when libmsa.so is missing: no fallback exists
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _randn(gen, *shape, dtype=torch.float32, scale=1.0):
+    return (torch.randn(*shape, generator=gen) * scale).to(dtype)
+
+
+def _dev(x):
+    return torch.as_tensor(x).to(DEV)
+
+
+# ==========================================================================
+# stage 1: pooling
+# ==========================================================================
+
+def _pool_check(k, v, kr, lens, P, dtype, what, theta=THETA):
+    tok_off = synth.token_offsets(lens)
+    pool_off = synth.row_offsets(lens, P)
+    kv_g, kr_g = msa.pool_encode(_dev(k), _dev(v), _dev(kr), _dev(tok_off), _dev(pool_off), P, theta,
+                                 int(pool_off[-1]))
+    torch.cuda.synchronize()
+    kv_r, kr_r, off_r = oracle.pool(np64(k), np64(v), np64(kr), tok_off, P, theta, "f64")
+    assert np.array_equal(off_r, pool_off)
+    check_pool(np64(kv_g[:, 0]), kv_r[:, 0], dtype, what + " K_bar")
+    check_pool(np64(kv_g[:, 1]), kv_r[:, 1], dtype, what + " V_bar")
+    check_pool(np64(kr_g), kr_r, dtype, what + " Kr_bar")
+
+
+def test_pool_tiny_config_fp32():
+    cfg = synth.config(1)
+    _say("pool: 64 docs x 512 tokens fp32, pool 64")
+    bank = synth.raw_bank(cfg)
+    _pool_check(bank["k"], bank["v"], bank["kr"], bank["lens"], cfg.pool, torch.float32, "tiny")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("P", [1, 7, 64, 100])
+def test_pool_ragged_documents(dtype, P):
+    g = torch.Generator().manual_seed(1000 + P)
+    lens = np.concatenate([[1, 2, P, P + 1, 2 * P - 1], torch.randint(1, 300, (20,), generator=g).numpy()])
+    n = int(lens.sum())
+    _say(f"pool: ragged {len(lens)} docs ({n} tokens), P={P}, {dtype}")
+    _pool_check(_randn(g, n, 8, 128, dtype=dtype), _randn(g, n, 8, 128, dtype=dtype),
+                _randn(g, n, 8, 128, dtype=dtype), lens, P, dtype, f"ragged P={P}")
+
+
+def test_pool_small_heads_and_long_document():
+    # one 70,000-token document: in-document positions far beyond one RoPE period
+    g = torch.Generator().manual_seed(7)
+    lens = np.array([70_000, 3, 1025])
+    n = int(lens.sum())
+    _say("pool: 70K-token document, Hkv=1, D=64, Hr=2, dr=64, P=1024, fp32")
+    _pool_check(_randn(g, n, 1, 64), _randn(g, n, 1, 64), _randn(g, n, 2, 64), lens, 1024, torch.float32,
+                "long doc", theta=1e4)
+
+
+def test_pool_constant_chunk_and_zero_input_on_gpu():
+    g = torch.Generator().manual_seed(3)
+    lens = np.array([64, 64, 10])
+    c = _randn(g, 1, 8, 128, dtype=torch.bfloat16)
+    v = c.repeat(138, 1, 1)
+    _say("pool: constant V/Kr chunks pool to themselves; zero K pools to zero")
+    kv_g, kr_g = msa.pool_encode(_dev(torch.zeros(138, 8, 128, dtype=torch.bfloat16)), _dev(v), _dev(v),
+                                 _dev(synth.token_offsets(lens)), _dev(synth.row_offsets(lens, 64)), 64, THETA, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(kv_g[:, 1].cpu(), c.repeat(3, 1, 1))
+    assert torch.equal(kr_g.cpu(), c.repeat(3, 1, 1))
+    assert torch.count_nonzero(kv_g[:, 0]).item() == 0
+
+
+def test_pool_routing_layer_config_sampled():
+    """Full 2048-document bf16 bank (~1.3M tokens, lengths U[256,1024]);
+    32 sampled documents checked against the oracle one by one."""
+    cfg = synth.config(2)
+    _say("pool: routing-layer bank, 2048 docs, bf16, sampled docs")
+    bank = synth.raw_bank(cfg, device=DEV)
+    lens = bank["lens"]
+    pool_off = synth.row_offsets(lens, cfg.pool)
+    kv_g, kr_g = msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], _dev(pool_off),
+                                 cfg.pool, cfg.rope_theta, int(pool_off[-1]))
+    torch.cuda.synchronize()
+    tok_off = synth.token_offsets(lens)
+    rng = np.random.default_rng(2)
+    for d in np.concatenate([[0, len(lens) - 1], rng.choice(len(lens), 30, replace=False)]):
+        a, b = tok_off[d], tok_off[d + 1]
+        kb, vb, rb = oracle.pool_doc(np64(bank["k"][a:b]), np64(bank["v"][a:b]), np64(bank["kr"][a:b]),
+                                     cfg.pool, cfg.rope_theta, "f64")
+        r0, r1 = pool_off[d], pool_off[d + 1]
+        check_pool(np64(kv_g[r0:r1, 0]), kb, torch.bfloat16, f"doc {d} K_bar")
+        check_pool(np64(kv_g[r0:r1, 1]), vb, torch.bfloat16, f"doc {d} V_bar")
+        check_pool(np64(kr_g[r0:r1]), rb, torch.bfloat16, f"doc {d} Kr_bar")
+
+
+# ==========================================================================
+# stage 2: routing
+# ==========================================================================
+
+def _route_check(kr_pooled, pool_off, qr, k, what):
+    idx, sc, dsc = msa.route(qr, kr_pooled, _dev(pool_off), k)
+    torch.cuda.synchronize()
+    ref = oracle.doc_scores(np64(qr), np64(kr_pooled), pool_off)
+    check_scores(np64(dsc), ref, what)
+    check_topk(np64(idx), ref, k, what)
+    check_topk_order(np64(idx), np64(sc), what)
+    assert np.array_equal(np64(sc), np.take_along_axis(np64(dsc), np64(idx), 1))
+    return np64(idx), ref
+
+
+def _ragged_bank(gen, n_docs, max_rows, hr, dr, dtype):
+    rows = torch.randint(1, max_rows + 1, (n_docs,), generator=gen).numpy()
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    return _randn(gen, int(off[-1]), hr, dr, dtype=dtype).to(DEV), off
+
+
+def test_route_tiny_config_fp32():
+    cfg = synth.config(1)
+    _say("route: tiny config, fp32, 16 query tokens, top-4")
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    g = torch.Generator().manual_seed(11)
+    kr = _randn(g, int(off[-1]), cfg.n_router_heads, cfg.router_dim).to(DEV)
+    qr = synth.router_queries(cfg).to(DEV)
+    _route_check(kr, off, qr, cfg.top_k, "tiny fp32")
+
+
+@pytest.mark.parametrize("hr,dr", [(8, 128), (4, 64), (1, 128), (16, 64), (2, 128)])
+@pytest.mark.parametrize("b,tq", [(1, 1), (8, 1), (2, 4), (3, 2), (1, 8)])
+def test_route_matrix_core_path(hr, dr, b, tq):
+    g = torch.Generator().manual_seed(hr * 100 + dr + b * 7 + tq)
+    kr, off = _ragged_bank(g, 700, 5, hr, dr, torch.bfloat16)       # ~2100 rows, ragged last tile
+    qr = _randn(g, b, tq, hr, dr, dtype=torch.bfloat16).to(DEV)
+    _say(f"route: MFMA path Hr={hr} dr={dr} B={b} Tq={tq} rows={off[-1]}")
+    _route_check(kr, off, qr, 16, f"mfma {hr}x{dr} B{b} Tq{tq}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("b,tq", [(1, 16), (4, 3), (9, 1)])
+def test_route_vector_path(dtype, b, tq):
+    g = torch.Generator().manual_seed(b * 31 + tq)
+    kr, off = _ragged_bank(g, 500, 4, 8, 128, dtype)
+    qr = _randn(g, b, tq, 8, 128, dtype=dtype).to(DEV)
+    _say(f"route: vector path B={b} Tq={tq} {dtype}")
+    _route_check(kr, off, qr, 8, f"valu B{b} Tq{tq}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_route_ties_go_to_lower_document_id(dtype):
+    g = torch.Generator().manual_seed(5)
+    kr, off = _ragged_bank(g, 300, 3, 8, 128, dtype)
+    hot = _randn(g, 1, 8, 128, dtype=dtype).to(DEV)
+    twins = [17, 18, 90, 200, 299]
+    for d in twins:                              # identical best rows: bit-identical scores
+        kr[off[d]] = hot[0]
+    qr = hot[None].clone()
+    _say(f"route: exact ties across documents {twins}, {dtype}")
+    idx, sc, dsc = msa.route(qr, kr, _dev(off), 8)
+    torch.cuda.synchronize()
+    idx = np64(idx)[0]
+    assert idx[:5].tolist() == twins
+    assert len(set(np64(sc)[0, :5].tolist())) == 1
+    check_topk(idx[None], oracle.doc_scores(np64(qr), np64(kr), off), 8, "ties")
+
+
+def test_route_all_documents_and_degenerate_rows():
+    g = torch.Generator().manual_seed(6)
+    kr, off = _ragged_bank(g, 37, 3, 8, 128, torch.bfloat16)
+    kr[off[4]:off[5]] = 0                        # a document of zero vectors scores exactly 0
+    qr = _randn(g, 2, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+    _say("route: k = n_docs (a permutation), a zero-vector document")
+    idx, ref = _route_check(kr, off, qr, 37, "k=all")
+    for row in idx:
+        assert sorted(row.tolist()) == list(range(37))
+    dsc = msa.route(qr, kr, _dev(off), 1)[2]
+    assert np64(dsc)[:, 4].tolist() == [0.0, 0.0]
+
+
+def test_route_single_document_bank():
+    g = torch.Generator().manual_seed(8)
+    kr, off = _ragged_bank(g, 1, 1, 8, 128, torch.bfloat16)
+    qr = _randn(g, 1, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+    _say("route: one document with one row")
+    idx, ref = _route_check(kr, off, qr, 1, "single")
+    assert idx.tolist() == [[0]]
+
+
+def test_route_needle_bank_full_size():
+    """16M-token bank (32768 lognormal docs, ~276K pooled rows, bf16), 8
+    queries of one token; each planted needle (cosine 0.6) is in its top-16
+    and every document score matches the oracle."""
+    cfg = synth.config(3)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    _say(f"route: needle bank, {len(lens)} docs, {off[-1]} rows, B=8")
+    kr = synth.pooled_router_bank(cfg, lens, device=DEV)
+    qr = synth.router_queries(cfg, device=DEV)
+    needles = synth.plant_needles(cfg, qr, kr, off)
+    idx, sc, dsc = msa.route(qr, kr, _dev(off), cfg.top_k)
+    torch.cuda.synchronize()
+    idx = np64(idx)
+    for b, d in enumerate(needles):
+        assert d in idx[b].tolist(), f"needle {d} missing for query {b}"
+        assert idx[b, 0] == d
+    qn = np64(qr)
+    ref = np.empty((cfg.batch, len(lens)))
+    step = 4096
+    for d0 in range(0, len(lens), step):
+        d1 = min(d0 + step, len(lens))
+        ref[:, d0:d1] = oracle.doc_scores(qn, np64(kr[off[d0]:off[d1]]), off[d0:d1 + 1] - off[d0])
+    check_scores(np64(dsc), ref, "needle bank")
+    check_topk(idx, ref, cfg.top_k, "needle bank")
+    assert np.all(np.abs(ref[np.arange(cfg.batch), needles] - 0.6) < 5e-3)
+
+
+@pytest.mark.slow
+def test_route_100m_bank_sampled():
+    """100M-token bank (195,313 docs x 512 tokens = 1,562,504 pooled rows,
+    3.2 GB bf16) at one query token: the selected documents and 4096 sampled
+    others are scored by the oracle one by one."""
+    cfg = synth.config(4)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    _say(f"route: 100M-token bank, {off[-1]} rows")
+    kr = synth.pooled_router_bank(cfg, lens, device=DEV)
+    qr = synth.router_queries(cfg, device=DEV)
+    idx, sc, dsc = msa.route(qr, kr, _dev(off), cfg.top_k)
+    torch.cuda.synchronize()
+    idx = np64(idx)[0]
+    dsc = np64(dsc)[0]
+    rng = np.random.default_rng(4)
+    sample = np.unique(np.concatenate([idx, rng.choice(len(lens), 4096, replace=False), [0, len(lens) - 1]]))
+    qn = np64(qr)
+    ref = np.array([oracle.doc_scores(qn, np64(kr[off[d]:off[d + 1]]), [0, off[d + 1] - off[d]])[0, 0]
+                    for d in sample])
+    check_scores(dsc[sample], ref, "100M sampled")
+    sel = np.isin(sample, idx)
+    # every selected document beats every sampled unselected one, up to tau
+    assert ref[sel].min() >= ref[~sel].max() - TAU
+    check_topk_order(idx[None], np64(sc))
+
+
+# ==========================================================================
+# stage 3: decode
+# ==========================================================================
+
+def _decode_check(b, hq, hkv, d, mem_cap, loc_cap, mem_len, loc_len, pos, dtype, what, mem_scale=1.0, seed=0,
+                  theta=THETA):
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, b, hq, d, dtype=dtype)
+    mem = None
+    if mem_cap:
+        mem = torch.randn(b, mem_cap, 2, hkv, d, generator=g)
+        mem[:, :, 0] *= mem_scale
+        mem = mem.to(dtype)
+    lk = _randn(g, b, loc_cap, hkv, d, dtype=dtype)
+    lv = _randn(g, b, loc_cap, hkv, d, dtype=dtype)
+    i32 = lambda x: torch.as_tensor(np.asarray(x, dtype=np.int32)).to(DEV)  # noqa: E731
+    out, lse = msa.sparse_decode(_dev(q), None if mem is None else _dev(mem), i32(mem_len), _dev(lk), _dev(lv),
+                                 i32(loc_len), i32(pos), theta)
+    torch.cuda.synchronize()
+    mem_np = np64(mem) if mem is not None else np.zeros((b, 0, 2, hkv, d))
+    ro, rl = oracle.decode(np64(q), mem_np, mem_len, np64(lk), np64(lv), loc_len, pos, theta, None, storage(dtype))
+    check_decode(np64(out), ro, dtype, what)
+    gl = np64(lse)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.all(np.abs(gl[fin] - rl[fin]) <= 1e-3), what
+    return np64(out), gl
+
+
+def test_decode_tiny_config_fp32():
+    _say("decode: 8/2 x 64 fp32, memory 32 rows, local 128")
+    _decode_check(1, 8, 2, 64, 32, 128, [32], [128], [4], torch.float32, "tiny")
+
+
+@pytest.mark.parametrize("mem_scale", [1.0, 8.0])
+def test_decode_100m_config_shape_bf16(mem_scale):
+    _say(f"decode: 32/8 x 128 bf16, memory 128 rows (K x{mem_scale}), local 4096")
+    _decode_check(1, 32, 8, 128, 128, 4096, [128], [4096], [16], torch.bfloat16, "100M shape",
+                  mem_scale=mem_scale, seed=int(mem_scale))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_ragged_batch(dtype):
+    _say(f"decode: batch of 5 with ragged lengths, {dtype}")
+    _decode_check(5, 32, 8, 128, 200, 300, [0, 5, 128, 77, 200], [1, 64, 65, 300, 0], [0, 3, 16, 1000, 7],
+                  dtype, "ragged", mem_scale=8.0, seed=3)
+
+
+def test_decode_head_dim_64_and_group_8():
+    _say("decode: D=64, 8 query heads per KV head, bf16")
+    _decode_check(2, 16, 2, 64, 64, 130, [64, 10], [130, 1], [16, 5], torch.bfloat16, "d64 g8", mem_scale=4.0)
+
+
+def test_decode_empty_contexts():
+    _say("decode: no keys at all, and memory only")
+    out, lse = _decode_check(2, 8, 2, 64, 16, 8, [0, 16], [0, 0], [0, 4], torch.float32, "empty")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    _say("decode: no memory buffer (capacity 0)")
+    _decode_check(1, 8, 2, 64, 0, 70, [0], [70], [3], torch.float32, "no memory")
+
+
+def test_decode_large_position_offset():
+    _say("decode: position offset 1e6 (RoPE angle reduction)")
+    _decode_check(1, 8, 2, 128, 8, 100, [8], [100], [1_000_000], torch.float32, "big offset", mem_scale=4.0)
+
+
+def test_decode_local_only_is_offset_invariant():
+    g = torch.Generator().manual_seed(9)
+    q = _randn(g, 1, 32, 128, dtype=torch.bfloat16).to(DEV)
+    lk = _randn(g, 1, 500, 8, 128, dtype=torch.bfloat16).to(DEV)
+    lv = _randn(g, 1, 500, 8, 128, dtype=torch.bfloat16).to(DEV)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=DEV)  # noqa: E731
+    _say("decode: empty memory, offsets 0 and 12345 agree")
+    a, _ = msa.sparse_decode(q, None, i32([0]), lk, lv, i32([500]), i32([0]), THETA)
+    b, _ = msa.sparse_decode(q, None, i32([0]), lk, lv, i32([500]), i32([12345]), THETA)
+    torch.cuda.synchronize()
+    check_decode(np64(a), np64(b), torch.bfloat16, "offset invariance")
+
+
+# ==========================================================================
+# context assembly (gather)
+# ==========================================================================
+
+def _bank_with_host_tier(gen, n_docs, max_rows, hkv, d, dtype):
+    rows = torch.randint(1, max_rows + 1, (n_docs,), generator=gen).numpy()
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    host_kv = _randn(gen, int(off[-1]), 2, hkv, d, dtype=dtype).pin_memory()
+    kr = _randn(gen, int(off[-1]), 8, 128, dtype=torch.bfloat16).to(DEV)
+    return off, host_kv, kr
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gather_is_byte_exact_in_rank_order(dtype):
+    g = torch.Generator().manual_seed(21)
+    off, host_kv, kr = _bank_with_host_tier(g, 400, 9, 8, 128, dtype)
+    qr = _randn(g, 3, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+    k, cap = 12, 40
+    asm = msa.Assembly.allocate(host_kv, torch.as_tensor(off), 3, k, cap, DEV, copy_stream=torch.cuda.Stream())
+    _say(f"gather: 3 queries, top-{k}, cap {cap} rows, {dtype}")
+    idx, _, _ = msa.route(qr, kr, _dev(off), k, assembly=asm)
+    torch.cuda.synchronize()
+    idx = np64(idx)
+    assert np.array_equal(asm.host_topk_idx.numpy(), idx)
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    src = host_kv.view(bits).numpy()
+    ref_mem, ref_len, ref_taken = oracle.assemble(src, off, idx, cap)
+    got = asm.mem_kv.view(bits).cpu().numpy()
+    assert np.array_equal(np64(asm.mem_len), ref_len)
+    assert np.array_equal(asm.host_mem_len.numpy(), ref_len)
+    assert np.array_equal(asm.host_mem_docs.numpy(), ref_taken)
+    for b in range(3):
+        assert np.array_equal(got[b, :ref_len[b]], ref_mem[b, :ref_len[b]])
+    assert ref_taken.min() < k, "the capacity should force a drop in this case"
+    assert np.array_equal(ref_len, [int(off[idx[b, :ref_taken[b]] + 1].sum() - off[idx[b, :ref_taken[b]]].sum())
+                                    for b in range(3)])
+
+
+def test_gather_append_mode():
+    g = torch.Generator().manual_seed(22)
+    off, host_kv, kr = _bank_with_host_tier(g, 300, 6, 8, 128, torch.bfloat16)
+    asm = msa.Assembly.allocate(host_kv, torch.as_tensor(off), 2, 4, 200, DEV)
+    src = host_kv.view(torch.int16).numpy()
+    ref_mem = np.zeros((2, 200) + src.shape[1:], dtype=np.int16)
+    ref_len = np.zeros(2, dtype=np.int64)
+    for rnd in range(3):
+        qr = _randn(g, 2, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+        asm.append = rnd > 0
+        _say(f"gather: append round {rnd}")
+        idx, _, _ = msa.route(qr, kr, _dev(off), 4, assembly=asm)
+        torch.cuda.synchronize()
+        ref_mem, ref_len, _ = oracle.assemble(src, off, np64(idx), 200, start_len=ref_len, mem=ref_mem)
+        assert np.array_equal(asm.host_mem_len.numpy(), ref_len)
+        got = asm.mem_kv.view(torch.int16).cpu().numpy()
+        for b in range(2):
+            assert np.array_equal(got[b, :ref_len[b]], ref_mem[b, :ref_len[b]])
+
+
+# ==========================================================================
+# end to end
+# ==========================================================================
+
+def _chain(cfg, lens, k, mem_cap, P, pos_offset):
+    bank = synth.raw_bank(cfg, lens=lens)
+    tok_off = synth.token_offsets(lens)
+    pool_off = synth.row_offsets(lens, P)
+    n_pool = int(pool_off[-1])
+    kv_g, kr_g = msa.pool_encode(_dev(bank["k"]), _dev(bank["v"]), _dev(bank["kr"]), _dev(tok_off),
+                                 _dev(pool_off), P, cfg.rope_theta, n_pool)
+    host_kv = kv_g.cpu().pin_memory()             # the content tier lives in pinned host memory
+    qr = synth.router_queries(cfg).to(DEV)
+    asm = msa.Assembly.allocate(host_kv, torch.as_tensor(pool_off), cfg.batch, k, mem_cap, DEV)
+    idx, _, dsc = msa.route(qr, kr_g, _dev(pool_off), k, assembly=asm)
+    q = synth.decode_queries(cfg).to(DEV)
+    lk, lv = synth.local_context(cfg)
+    loc_len = np.full(cfg.batch, cfg.local_len, dtype=np.int32)
+    pos = np.full(cfg.batch, pos_offset, dtype=np.int32)
+    out, lse = msa.sparse_decode(q, asm.mem_kv, asm.mem_len, _dev(lk), _dev(lv), _dev(loc_len), _dev(pos),
+                                 cfg.rope_theta)
+    torch.cuda.synchronize()
+
+    kv_u, kr_u, _ = oracle.pool(np64(bank["k"]), np64(bank["v"]), np64(bank["kr"]), tok_off, P, cfg.rope_theta,
+                                "f64")
+    check_pool(np64(kv_g[:, 0]), kv_u[:, 0], cfg.torch_dtype, "chain K_bar")
+    kv_r = oracle.round_to_storage(kv_u, storage(cfg.torch_dtype))
+    kr_r = oracle.round_to_storage(kr_u, storage(cfg.torch_dtype))
+    dsc_r = oracle.doc_scores(np64(qr), kr_r, pool_off)
+    check_scores(np64(dsc), dsc_r, "chain scores")
+    check_topk(np64(idx), dsc_r, k, "chain top-k")
+    # decode is checked on the GPU-selected documents (oracle-pooled rows)
+    mem_r, mlen_r, _ = oracle.assemble(kv_r, pool_off, np64(idx), mem_cap)
+    assert np.array_equal(np64(asm.mem_len), mlen_r)
+    ro, _ = oracle.decode(np64(q), mem_r, mlen_r, np64(lk), np64(lv), loc_len, pos, cfg.rope_theta, None,
+                          storage(cfg.torch_dtype))
+    check_decode(np64(out), ro, cfg.torch_dtype, "chain decode")
+    return kv_r, kv_g, out
+
+
+def test_end_to_end_tiny_config():
+    cfg = synth.config(1)
+    _say("chain: tiny config pool -> route -> gather -> decode")
+    _chain(cfg, synth.doc_lengths(cfg), cfg.top_k, 64, cfg.pool, cfg.top_k)
+
+
+def test_end_to_end_bf16_ragged():
+    cfg = synth.config(2, batch=2, q_tokens=3, local_len=300)
+    lens = np.random.default_rng(5).integers(1, 500, 60)
+    _say("chain: bf16 ragged bank, 2 queries x 3 tokens")
+    _chain(cfg, lens, 6, 64, 64, 6)
+
+
+def test_dense_special_case_equals_sdpa():
+    """Pool size 1 and k = all documents: the whole path is dense attention
+    over [every document's rotated keys ; the locally rotated keys], checked
+    against torch's scaled_dot_product_attention in float64 on the CPU."""
+    cfg = synth.config(1, local_len=37)
+    lens = np.array([3, 9, 5, 1, 7, 4])
+    _say("chain: P=1, k=n_docs vs dense SDPA")
+    kv_r, kv_g, out = _chain(cfg, lens, len(lens), int(lens.sum()), 1, len(lens))
+    bank = synth.raw_bank(cfg, lens=lens)
+    tok_off = synth.token_offsets(lens)
+    keys = [oracle.rope(np64(bank["k"][tok_off[i]:tok_off[i + 1]]), np.arange(lens[i]), cfg.rope_theta)
+            for i in range(len(lens))]
+    lk, lv = synth.local_context(cfg)
+    o = len(lens)
+    keys.append(oracle.rope(np64(lk[0]), o + np.arange(cfg.local_len), cfg.rope_theta))
+    vals = [np64(bank["v"][tok_off[i]:tok_off[i + 1]]) for i in range(len(lens))] + [np64(lv[0])]
+    rep = cfg.n_q_heads // cfg.n_kv_heads
+    kk = torch.from_numpy(np.concatenate(keys)).permute(1, 0, 2).repeat_interleave(rep, 0).contiguous()
+    vv = torch.from_numpy(np.concatenate(vals)).permute(1, 0, 2).repeat_interleave(rep, 0).contiguous()
+    q = synth.decode_queries(cfg)
+    qq = torch.from_numpy(oracle.rope(np64(q[0])[None], [o + cfg.local_len - 1], cfg.rope_theta)[0])[:, None, :]
+    want = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[:, 0].numpy()
+    check_decode(np64(out)[0], want, torch.float32, "dense special case")
