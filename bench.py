@@ -10,8 +10,9 @@ path on fresh synthetic inputs:
   1. pool: msa_pool_encode of a batch of 64 new documents x 512 tokens
      (document-wise RoPE + chunk means of K/V/Kr);
   2. route: msa_route with one query token - cosine scan of the whole bank,
-     head mean, per-document max, top-16, then the host-driven copy of the
-     16 selected documents' pooled K/V from pinned memory;
+     head mean, per-document max, top-16, then the device-side copy of the
+     16 selected documents' pooled K/V from mapped pinned memory (the
+     host-driven hipMemcpyAsync mode is timed beside it for latency);
   3. decode: msa_sparse_decode, GQA 32/8 x 128 over [128 memory rows ;
      4096 local tokens] with the query offset by k = 16.
 Inputs are resident before the timed region.  Prints one JSON line.
@@ -109,7 +110,9 @@ def main():
     k = cfg.top_k
     mem_cap = k * (512 // cfg.pool)
     copy_stream = torch.cuda.Stream()
-    asm = msa.Assembly.allocate(host_kv, pool_off_h, cfg.batch, k, mem_cap, dev, copy_stream=copy_stream)
+    asm = msa.Assembly.allocate(host_kv, pool_off_h, cfg.batch, k, mem_cap, dev, mode="kernel")
+    asm_copies = msa.Assembly.allocate(host_kv, pool_off_h, cfg.batch, k, mem_cap, dev, copy_stream=copy_stream,
+                                       mode="copies")
     loc_len = torch.full((cfg.batch,), cfg.local_len, dtype=torch.int32, device=dev)
     pos = torch.full((cfg.batch,), k, dtype=torch.int32, device=dev)
     rws = torch.empty(msa.route_workspace_bytes(cfg.torch_dtype, cfg.batch, 1, cfg.n_router_heads, cfg.router_dim,
@@ -151,23 +154,29 @@ def main():
     scan_ms = np.array([scan_ev.elapsed_ms(j) for j in range(K)])
     dec_ms = np.array([dec_ev.elapsed_ms(j) for j in range(K)])
 
-    # route + decode latency per step (synchronised each step)
-    lat = []
-    for i in range(W + K, n_steps):
-        torch.cuda.synchronize()
-        a = time.perf_counter()
-        msa.route(qrs[i], kr, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=asm, stream=stream)
-        msa.sparse_decode(qs[i], asm.mem_kv, asm.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
-                          stream=stream)
-        torch.cuda.synchronize()
-        lat.append((time.perf_counter() - a) * 1e3)
-    lat = np.array(lat)
+    # route + decode latency per step (synchronised each step), both assembly modes
+    lat = {}
+    for name, a in (("kernel", asm), ("copies", asm_copies)):
+        vals = []
+        for i in range(W + K, n_steps):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            msa.route(qrs[i], kr, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=a, stream=stream)
+            msa.sparse_decode(qs[i], a.mem_kv, a.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
+                              stream=stream)
+            torch.cuda.synchronize()
+            vals.append((time.perf_counter() - t) * 1e3)
+        lat[name] = np.array(vals)
+    log(f"route+decode p50: kernel gather {np.median(lat['kernel']):.3f} ms, "
+        f"copy gather {np.median(lat['copies']):.3f} ms")
 
     scan_bytes = n_pool * cfg.n_router_heads * cfg.router_dim * 2 + cfg.n_router_heads * cfg.router_dim * 2
     scan_avg_s = scan_ms.mean() / 1e3
     achieved = scan_bytes / scan_avg_s / 1e9
     value = cfg.batch * bank_tokens * K / elapsed
     dec_bytes = (mem_cap + cfg.local_len) * cfg.n_kv_heads * cfg.head_dim * 2 * 2
+    # route + decode floor: bank + decode K/V at HBM peak, the 16 documents over a 64 GB/s host link
+    t_floor_ms = (scan_bytes + dec_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3 + mem_cap * 4096 / 64e9 * 1e3
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -207,9 +216,11 @@ def main():
             "scan_bytes": scan_bytes,
         },
         "latency_ms": {
-            "route_decode_p50": float(np.percentile(lat, 50)),
-            "route_decode_p90": float(np.percentile(lat, 90)),
-            "route_decode_p99": float(np.percentile(lat, 99)),
+            "route_decode_p50": float(np.percentile(lat["kernel"], 50)),
+            "route_decode_p90": float(np.percentile(lat["kernel"], 90)),
+            "route_decode_p99": float(np.percentile(lat["kernel"], 99)),
+            "route_decode_p50_copy_gather": float(np.percentile(lat["copies"], 50)),
+            "roofline_floor": float(t_floor_ms),
             "decode_attention_us": float(dec_ms.mean() * 1e3),
             "decode_achieved_GBs": float(dec_bytes / (dec_ms.mean() / 1e3) / 1e9),
         },

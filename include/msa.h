@@ -121,15 +121,28 @@ int msa_pool_encode(const msa_pool_args *args, void *stream);
  *
  * Assembly (when host_kv != NULL): the selected documents' pooled rows
  * host_kv[doc_pool_off[d] .. doc_pool_off[d+1]) are copied, in rank order,
- * into mem_kv[b, mem_len0[b] ...] where mem_len0[b] is host_mem_len[b] when
- * `append` is set and 0 otherwise.  A document that does not fit in
- * mem_cap rows is dropped together with every lower-ranked one.  This path
- * BLOCKS the calling thread until the top-k indices are in host_topk_idx,
- * then enqueues one hipMemcpyAsync per document on copy_stream, writes the
- * new lengths to host_mem_len / host_mem_docs and copies them to mem_len,
- * and makes `stream` wait for those copies (a later msa_sparse_decode on
- * `stream` sees the assembled memory).
+ * into mem_kv[b, L0 ...] where L0 is the current length when `append` is set
+ * and 0 otherwise.  A document that does not fit in mem_cap rows is dropped
+ * together with every lower-ranked one.  After the call, mem_len[b] is the
+ * new length, and a later msa_sparse_decode on `stream` sees the memory.
+ * The content tier is not in HBM: it is "fetched when selected" from host
+ * memory, as the sources describe the tiered storage.  Two modes:
+ *  MSA_GATHER_COPIES (0): BLOCKS the calling thread until the top-k indices
+ *    are in host_topk_idx, enqueues one hipMemcpyAsync per document on
+ *    copy_stream, writes host_mem_len / host_mem_docs (current length read
+ *    from host_mem_len when appending), copies the lengths to mem_len and
+ *    makes `stream` wait for the copies.  host_kv may be any pinned memory.
+ *  MSA_GATHER_KERNEL (1): fully asynchronous.  The top-k kernel plans the
+ *    copies on the device (current length read from mem_len when
+ *    appending) and a gather kernel on `stream` reads the selected rows
+ *    straight from host_kv, which must be device-mapped pinned memory
+ *    (hipHostMalloc; checked with hipHostGetDevicePointer).  host_topk_idx,
+ *    host_mem_len, host_mem_docs and copy_stream are unused (may be NULL).
+ * In both modes host_kv must hold n_pool rows.  The host buffers of the copy
+ * mode must not be modified until `stream` has passed this call.
  * ------------------------------------------------------------------------ */
+typedef enum { MSA_GATHER_COPIES = 0, MSA_GATHER_KERNEL = 1 } msa_gather_mode;
+
 typedef struct {
   int32_t dtype;            /* msa_dtype of qr and kr_pooled                */
   int32_t batch;            /* B >= 1 independent queries                   */
@@ -155,14 +168,15 @@ typedef struct {
   int32_t n_kv_heads;
   int32_t head_dim;
   int32_t mem_cap;                  /* rows per query in mem_kv             */
-  int32_t append;                   /* 1: append after host_mem_len[b]      */
-  int32_t reserved1;
+  int32_t append;                   /* 1: append after the current length   */
+  int32_t gather_mode;              /* msa_gather_mode                      */
   void *mem_kv;                     /* device [B, mem_cap, 2, Hkv, D]       */
-  int32_t *mem_len;                 /* device out [B]                       */
-  int32_t *host_topk_idx;           /* pinned host out [B, k]               */
-  int32_t *host_mem_len;            /* pinned host in/out [B]               */
-  int32_t *host_mem_docs;           /* pinned host out [B] docs taken; opt. */
-  void *copy_stream;                /* hipStream_t for the copies           */
+  int32_t *mem_len;                 /* device [B]: out; in when appending   */
+                                    /*   in MSA_GATHER_KERNEL mode          */
+  int32_t *host_topk_idx;           /* pinned host out [B, k]     (copies)  */
+  int32_t *host_mem_len;            /* pinned host in/out [B]     (copies)  */
+  int32_t *host_mem_docs;           /* pinned host out [B]; opt.  (copies)  */
+  void *copy_stream;                /* hipStream_t for the copies (copies)  */
   /* profiling, optional: hipEvent_t values recorded on `stream` right before
    * and right after the bank-scan kernel; NULL to skip */
   void *prof_event_begin;

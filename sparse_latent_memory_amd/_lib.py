@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_CAPACITY, MSA_ERR_HIP = 0, -1, -2, -3, -4, -5
 MSA_F32, MSA_BF16 = 0, 1
+MSA_GATHER_COPIES, MSA_GATHER_KERNEL = 0, 1
 
 _DTYPE = {torch.float32: MSA_F32, torch.bfloat16: MSA_BF16}
 
@@ -47,7 +48,7 @@ class RouteArgs(ctypes.Structure):
         ("qr", P), ("kr_pooled", P), ("doc_pool_off", P), ("doc_scores", P), ("topk_idx", P),
         ("topk_score", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
         ("host_kv", P), ("host_doc_pool_off", P), ("kv_dtype", I32), ("n_kv_heads", I32), ("head_dim", I32),
-        ("mem_cap", I32), ("append", I32), ("reserved1", I32), ("mem_kv", P), ("mem_len", P), ("host_topk_idx", P),
+        ("mem_cap", I32), ("append", I32), ("gather_mode", I32), ("mem_kv", P), ("mem_len", P), ("host_topk_idx", P),
         ("host_mem_len", P), ("host_mem_docs", P), ("copy_stream", P),
         ("prof_event_begin", P), ("prof_event_end", P),
     ]
@@ -153,10 +154,15 @@ def route_workspace_bytes(dtype, batch, q_tokens, n_router_heads, router_dim, n_
 
 
 class Assembly:
-    """Buffers of the optional context-assembly part of msa_route."""
+    """Buffers of the optional context-assembly part of msa_route.
+
+    mode "kernel" (MSA_GATHER_KERNEL) or "copies" (MSA_GATHER_COPIES)."""
 
     def __init__(self, host_kv, host_doc_pool_off, mem_kv, mem_len, host_topk_idx, host_mem_len,
-                 host_mem_docs=None, append=False, copy_stream=None):
+                 host_mem_docs=None, append=False, copy_stream=None, mode="kernel"):
+        if mode not in ("kernel", "copies"):
+            raise ValueError(f"assembly mode {mode!r}")
+        self.mode = mode
         self.host_kv = host_kv
         self.host_doc_pool_off = host_doc_pool_off
         self.mem_kv = mem_kv
@@ -168,13 +174,14 @@ class Assembly:
         self.copy_stream = copy_stream
 
     @classmethod
-    def allocate(cls, host_kv, host_doc_pool_off, batch, top_k, mem_cap, device, copy_stream=None):
+    def allocate(cls, host_kv, host_doc_pool_off, batch, top_k, mem_cap, device, copy_stream=None,
+                 mode="kernel"):
         _, two, hkv, d = host_kv.shape
         mem_kv = torch.zeros((batch, mem_cap, two, hkv, d), dtype=host_kv.dtype, device=device)
         return cls(host_kv, host_doc_pool_off, mem_kv, torch.zeros(batch, dtype=torch.int32, device=device),
                    torch.zeros((batch, top_k), dtype=torch.int32, pin_memory=True),
                    torch.zeros(batch, dtype=torch.int32, pin_memory=True),
-                   torch.zeros(batch, dtype=torch.int32, pin_memory=True), copy_stream=copy_stream)
+                   torch.zeros(batch, dtype=torch.int32, pin_memory=True), copy_stream=copy_stream, mode=mode)
 
 
 def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, topk_score=None,
@@ -208,6 +215,7 @@ def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, to
         a.head_dim = asm.host_kv.shape[3]
         a.mem_cap = asm.mem_kv.shape[1]
         a.append = 1 if asm.append else 0
+        a.gather_mode = MSA_GATHER_KERNEL if asm.mode == "kernel" else MSA_GATHER_COPIES
         a.mem_kv = _ptr(asm.mem_kv)
         a.mem_len = _ptr(asm.mem_len)
         a.host_topk_idx = _ptr(asm.host_topk_idx)

@@ -11,8 +11,10 @@
 // Split-KV design: grid (split, kv head, query).  Each workgroup owns a
 // contiguous key range of one (query, KV head) and all Hq/Hkv query heads of
 // that group (they share every staged K/V tile).  Per 64-key tile:
-//   stage   K (local keys rotated at o + i on the way into LDS; memory keys are
-//           used as stored) and V into LDS as fp32, coalesced 16-byte loads;
+//   stage   K and V global loads are issued first (16 bytes per lane,
+//           coalesced); the RoPE phasors of the local keys are computed while
+//           they are in flight; local keys are rotated at o + i, memory keys
+//           used as stored; both land in LDS in the storage type;
 //   scores  wave w <-> query head, lane <-> key: dot(q', K[key]) from LDS;
 //   softmax online, wave-wide max/sum, exp2 with log2(e) folded into q';
 //   PV      wave w <-> query head, lane <-> D/64 output dims.
@@ -26,7 +28,9 @@ namespace msa {
 namespace {
 
 constexpr int kTile = 64;
+constexpr int kReseed = 16;    // tiles between exact RoPE phasor evaluations
 constexpr int kMaxGroup = 8;   // query heads per KV head handled per workgroup
+constexpr int kMaxSplit = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -41,18 +45,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+__global__ __launch_bounds__(256, 3) void decode_split_kernel(
     const T *__restrict__ q, const T *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
     const T *__restrict__ local_k, const T *__restrict__ local_v, const int32_t *__restrict__ local_len,
     const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc, float *__restrict__ part_ml,
     int Hq, int Hkv, int mem_cap, int local_cap, int split_len, int n_split, float scale_log2,
     double log2_theta) {
-  constexpr int VW = Elt<T>::kPerVec;
+  constexpr int VW = Elt<T>::kPerVec;     // elements per 16-byte vector
   constexpr int HALF = D / 2;
-  constexpr int KSTR = D + 4;             // padded LDS row (conflict-free row reads)
+  constexpr int KSTR = D + VW;            // padded LDS row of K (conflict-free row reads)
   constexpr int DPL = D / 64;             // output dims per lane
-  __shared__ __align__(16) float ks[kTile * KSTR];
-  __shared__ __align__(16) float vs[kTile * D];
+  constexpr int KCH = HALF / VW;          // 16-byte pair-chunks per key
+  constexpr int KTPT = kTile * KCH / 256; // K tasks per thread
+  constexpr int KSTEP = 256 / KCH;        // key stride between a thread's K tasks
+  constexpr int VCH = D / VW;             // 16-byte chunks per V row
+  constexpr int VTPT = kTile * VCH / 256;
+  constexpr int VSTEP = 256 / VCH;
+  __shared__ __align__(16) T ks[kTile * KSTR];
+  __shared__ __align__(16) T vs[kTile * D];
   __shared__ __align__(16) float qs[kMaxGroup * D];
   __shared__ float ps[kMaxGroup * kTile];
   __shared__ double omega[HALF];
@@ -101,59 +111,88 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int64_t mem_row = 2LL * Hkv * D;      // elements per pooled memory row
   const int64_t loc_row = (int64_t)Hkv * D;   // elements per local token
 
-  for (int kt = k0; kt < k1; kt += kTile) {
+  // Thread t always owns the VW rotate-half pairs cj.. of the keys
+  // kk0 + j*KSTEP of every tile, so the RoPE phasor of each (key, pair)
+  // advances by e^{i 64 omega} from one tile to the next: it is evaluated
+  // exactly (fp64 angle reduction) once every kReseed tiles and carried by
+  // complex multiplication in between.
+  const int cj = (threadIdx.x % KCH) * VW, kk0 = threadIdx.x / KCH;
+  const int vj = (threadIdx.x % VCH) * VW, vk0 = threadIdx.x / VCH;
+  float zc[KTPT][VW], zs[KTPT][VW], wc[VW], ws[VW];
+#pragma unroll
+  for (int e = 0; e < VW; ++e) rope_phasor((double)kTile, omega[cj + e], &wc[e], &ws[e]);
+
+  for (int kt = k0, tile = 0; kt < k1; kt += kTile, ++tile) {
     const int nk = min(kTile, k1 - kt);
-    __syncthreads();  // previous tile fully consumed (and qs written on the first pass)
-    // ---- stage K (rotated when local) ----
-    constexpr int KCH = HALF / VW;   // 16-byte pair-chunks per key
-    for (int task = threadIdx.x; task < kTile * KCH; task += blockDim.x) {
-      const int kk = task / KCH, cj = (task % KCH) * VW;
-      float xl[VW], xh[VW];
+    // ---- issue this tile's global loads ----
+    u32x4 kl[KTPT], kh[KTPT], vv[VTPT];
+#pragma unroll
+    for (int j = 0; j < KTPT; ++j) {
+      const int kk = kk0 + j * KSTEP, key = kt + kk;
       if (kk < nk) {
-        const int key = kt + kk;
-        if (key < M) {
-          const T *src = mem_kv + ((int64_t)b * mem_cap + key) * mem_row + (int64_t)g * D;
-          Elt<T>::unpack(ld16(src + cj), xl);
-          Elt<T>::unpack(ld16(src + cj + HALF), xh);
-        } else {
-          const int i = key - M;
-          const T *src = local_k + ((int64_t)b * local_cap + i) * loc_row + (int64_t)g * D;
-          float rl[VW], rh[VW];
-          Elt<T>::unpack(ld16(src + cj), rl);
-          Elt<T>::unpack(ld16(src + cj + HALF), rh);
-#pragma unroll
-          for (int e = 0; e < VW; ++e) {
-            float c, s;
-            rope_phasor((double)o + (double)i, omega[cj + e], &c, &s);
-            xl[e] = rl[e] * c - rh[e] * s;
-            xh[e] = rh[e] * c + rl[e] * s;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < VW; ++e) xl[e] = xh[e] = 0.f;
+        const T *src = key < M ? mem_kv + ((int64_t)b * mem_cap + key) * mem_row + (int64_t)g * D
+                               : local_k + ((int64_t)b * local_cap + (key - M)) * loc_row + (int64_t)g * D;
+        kl[j] = ld16(src + cj);
+        kh[j] = ld16(src + cj + HALF);
       }
-      float *dst = ks + kk * KSTR + cj;
-#pragma unroll
-      for (int e = 0; e < VW; ++e) { dst[e] = xl[e]; dst[e + HALF] = xh[e]; }
     }
-    // ---- stage V ----
-    constexpr int VCH = D / VW;
-    for (int task = threadIdx.x; task < kTile * VCH; task += blockDim.x) {
-      const int kk = task / VCH, cj = (task % VCH) * VW;
-      float x[VW];
+#pragma unroll
+    for (int j = 0; j < VTPT; ++j) {
+      const int kk = vk0 + j * VSTEP, key = kt + kk;
       if (kk < nk) {
-        const int key = kt + kk;
         const T *src = key < M ? mem_kv + ((int64_t)b * mem_cap + key) * mem_row + loc_row + (int64_t)g * D
                                : local_v + ((int64_t)b * local_cap + (key - M)) * loc_row + (int64_t)g * D;
-        Elt<T>::unpack(ld16(src + cj), x);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VW; ++e) x[e] = 0.f;
+        vv[j] = ld16(src + vj);
       }
-      float *dst = vs + kk * D + cj;
+    }
+    // ---- phasors while the loads are in flight ----
+    if (tile % kReseed == 0) {
 #pragma unroll
-      for (int e = 0; e < VW; ++e) dst[e] = x[e];
+      for (int j = 0; j < KTPT; ++j)
+#pragma unroll
+        for (int e = 0; e < VW; ++e)
+          rope_phasor((double)o - M + kt + kk0 + j * KSTEP, omega[cj + e], &zc[j][e], &zs[j][e]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KTPT; ++j)
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+          const float c = zc[j][e] * wc[e] - zs[j][e] * ws[e];
+          zs[j][e] = zs[j][e] * wc[e] + zc[j][e] * ws[e];
+          zc[j][e] = c;
+        }
+    }
+    __syncthreads();  // previous tile fully consumed (and qs written on the first pass)
+    // ---- K (rotated when local) and V into LDS ----
+#pragma unroll
+    for (int j = 0; j < KTPT; ++j) {
+      const int kk = kk0 + j * KSTEP, key = kt + kk;
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (kk < nk) {
+        lo = kl[j];
+        hi = kh[j];
+        if (key >= M) {
+          float xl[VW], xh[VW], rl[VW], rh[VW];
+          Elt<T>::unpack(lo, xl);
+          Elt<T>::unpack(hi, xh);
+#pragma unroll
+          for (int e = 0; e < VW; ++e) {
+            rl[e] = xl[e] * zc[j][e] - xh[e] * zs[j][e];
+            rh[e] = xh[e] * zc[j][e] + xl[e] * zs[j][e];
+          }
+          lo = Elt<T>::pack(rl);
+          hi = Elt<T>::pack(rh);
+        }
+      }
+      st16(ks + kk * KSTR + cj, lo);
+      st16(ks + kk * KSTR + cj + HALF, hi);
+    }
+#pragma unroll
+    for (int j = 0; j < VTPT; ++j) {
+      const int kk = vk0 + j * VSTEP;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (kk < nk) x = vv[j];
+      st16(vs + kk * D + vj, x);
     }
     __syncthreads();
 
@@ -164,17 +203,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       if (hh >= G) break;
       float logit = -INFINITY;
       if (lane < nk) {
-        const float *kr = ks + lane * KSTR;
+        const T *kr = ks + lane * KSTR;
         const float *qr = qs + hh * D;
-        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < D; i += 4) {
-          acc0 += qr[i] * kr[i];
-          acc1 += qr[i + 1] * kr[i + 1];
-          acc2 += qr[i + 2] * kr[i + 2];
-          acc3 += qr[i + 3] * kr[i + 3];
+        for (int i = 0; i < D; i += VW) {
+          float x[VW];
+          Elt<T>::unpack(*reinterpret_cast<const u32x4 *>(kr + i), x);
+#pragma unroll
+          for (int e = 0; e < VW; e += 2) {
+            a0 += qr[i + e] * x[e];
+            a1 += qr[i + e + 1] * x[e + 1];
+          }
         }
-        logit = (acc0 + acc1) + (acc2 + acc3);
+        logit = a0 + a1;
       }
       const float m_tile = wave_max(logit);
       const float m_new = fmaxf(m_run[r], m_tile);
@@ -190,9 +232,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       const float *pr = ps + hh * kTile;
       for (int kk = 0; kk < nk; ++kk) {
         const float w = pr[kk];
-        const float *vr = vs + kk * D + lane * DPL;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[r][i] += w * vr[i];
+        for (int i = 0; i < DPL; ++i) acc[r][i] += w * Elt<T>::get(vs + kk * D, lane * DPL + i);
       }
     }
   }
@@ -212,29 +253,76 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
+// Combine the splits of one (query, head).  Wave 0 forms the weights
+// 2^(m_s - max m) in LDS and their l-weighted sum; then every thread owns a
+// float4 of the output and a stride of splits, with all its loads issued
+// before the adds.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float *__restrict__ part_acc,
-                                                        const float *__restrict__ part_ml, T *__restrict__ out,
-                                                        float *__restrict__ lse, int n_split) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restrict__ part_acc,
+                                                          const float *__restrict__ part_ml, T *__restrict__ out,
+                                                          float *__restrict__ lse, int n_split) {
+  constexpr int NV = D / 4;               // float4 per output row
+  constexpr int NGRP = 256 / NV;          // split groups
+  __shared__ float w[kMaxSplit];
+  __shared__ float s_m, s_l;
+  __shared__ float4 part[NGRP][NV];
   const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
   const float *ml = part_ml + bh * n_split * 2;
-  float m = -INFINITY;
-  for (int s = 0; s < n_split; ++s) m = fmaxf(m, ml[2 * s]);
-  float L = 0.f, acc = 0.f;
-  if (m > -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
+  if (tid < 64) {
+    float m = -INFINITY;
+    for (int s = tid; s < n_split; s += 64) m = fmaxf(m, ml[2 * s]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int s = tid; s < n_split; s += 64) {
       const float ms = ml[2 * s];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - m);
-      L += w * ml[2 * s + 1];
-      acc += w * part_acc[(bh * n_split + s) * D + threadIdx.x];
+      const float ws = (ms == -INFINITY) ? 0.f : exp2f(ms - m);
+      w[s] = ws;
+      l += ws * ml[2 * s + 1];
+    }
+    l = wave_sum(l);
+    if (tid == 0) { s_m = m; s_l = l; }
+  }
+  __syncthreads();
+  const int v = tid % NV, grp = tid / NV;
+  const float4 *pa = reinterpret_cast<const float4 *>(part_acc + bh * n_split * D) + v;
+  float4 a = {0.f, 0.f, 0.f, 0.f};
+  int s = grp;
+  for (; s + 3 * NGRP < n_split; s += 4 * NGRP) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = pa[(int64_t)(s + u * NGRP) * NV];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float ws = w[s + u * NGRP];
+      a.x += ws * x[u].x; a.y += ws * x[u].y; a.z += ws * x[u].z; a.w += ws * x[u].w;
     }
   }
-  const float o = L > 0.f ? acc / L : 0.f;
-  Elt<T>::put(out, bh * D + threadIdx.x, o);
-  if (lse && threadIdx.x == 0) lse[bh] = L > 0.f ? (m + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  for (; s < n_split; s += NGRP) {
+    const float ws = w[s];
+    const float4 x = pa[(int64_t)s * NV];
+    a.x += ws * x.x; a.y += ws * x.y; a.z += ws * x.z; a.w += ws * x.w;
+  }
+  part[grp][v] = a;
+  __syncthreads();
+  const float L = s_l;
+  if (tid < NV) {
+    float4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g2 = 0; g2 < NGRP; ++g2) {
+      r.x += part[g2][tid].x; r.y += part[g2][tid].y; r.z += part[g2][tid].z; r.w += part[g2][tid].w;
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    Elt<T>::put(out, bh * D + 4 * tid + 0, r.x * inv);
+    Elt<T>::put(out, bh * D + 4 * tid + 1, r.y * inv);
+    Elt<T>::put(out, bh * D + 4 * tid + 2, r.z * inv);
+    Elt<T>::put(out, bh * D + 4 * tid + 3, r.w * inv);
+  }
+  if (lse && tid == 0) lse[bh] = L > 0.f ? (s_m + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
+// Keys per split: enough splits that batch * Hkv * n_split workgroups fill the
+// chip, in whole 64-key tiles.
 int choose_split_len(int32_t batch, int32_t mem_cap, int32_t local_cap) {
   const int64_t total = (int64_t)mem_cap + local_cap;
   int64_t len = (total * batch + 255) / 256;
@@ -250,6 +338,7 @@ hipError_t launch_t(const msa_decode_args &a, float *part_acc, float *part_ml, i
   hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a.prof_event_begin);
   hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a.prof_event_end);
   hipError_t e = hipSuccess;
+  if (n_split > kMaxSplit) return hipErrorInvalidValue;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(n_split, a.n_kv_heads, a.batch), dim3(256), 0, s,
                      reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.mem_kv), a.mem_len,
@@ -258,7 +347,7 @@ hipError_t launch_t(const msa_decode_args &a, float *part_acc, float *part_ml, i
                      a.local_cap, split_len, n_split, scale * kLog2e, log2(a.rope_theta));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.batch * a.n_q_heads), dim3(D), 0, s, part_acc,
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.batch * a.n_q_heads), dim3(256), 0, s, part_acc,
                      part_ml, reinterpret_cast<T *>(a.out), a.lse, n_split);
   return hipGetLastError();
 }

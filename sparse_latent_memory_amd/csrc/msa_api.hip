@@ -144,18 +144,34 @@ int msa_route(const msa_route_args *a, void *stream) {
     return fail(MSA_ERR_WORKSPACE, "msa_route: workspace needs %zu bytes (16-byte aligned), got %zu", need,
                 a->workspace ? a->workspace_bytes : (size_t)0);
   const bool assemble = a->host_kv != nullptr;
+  const bool kernel_gather = assemble && a->gather_mode == MSA_GATHER_KERNEL;
+  void *host_kv_dev = nullptr;
   if (assemble) {
-    if (!a->host_doc_pool_off || !a->mem_kv || !a->mem_len || !a->host_topk_idx || !a->host_mem_len)
-      return fail(MSA_ERR_INVALID_ARG, "msa_route: assembly needs host_doc_pool_off, mem_kv, mem_len, "
-                                       "host_topk_idx and host_mem_len");
+    if (a->gather_mode != MSA_GATHER_COPIES && a->gather_mode != MSA_GATHER_KERNEL)
+      return fail(MSA_ERR_INVALID_ARG, "msa_route: bad gather_mode %d", a->gather_mode);
+    if (!a->host_doc_pool_off || !a->mem_kv || !a->mem_len)
+      return fail(MSA_ERR_INVALID_ARG, "msa_route: assembly needs host_doc_pool_off, mem_kv and mem_len");
+    if (!kernel_gather && (!a->host_topk_idx || !a->host_mem_len))
+      return fail(MSA_ERR_INVALID_ARG, "msa_route: copy assembly needs host_topk_idx and host_mem_len");
     if (!dtype_ok(a->kv_dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_route: bad kv_dtype %d", a->kv_dtype);
     if (a->n_kv_heads < 1 || a->head_dim < 1 || a->mem_cap < 0)
       return fail(MSA_ERR_INVALID_ARG, "msa_route: assembly needs n_kv_heads, head_dim >= 1, mem_cap >= 0");
-    if (a->append) {
+    if (a->append && !kernel_gather) {
       for (int b = 0; b < a->batch; ++b)
         if (a->host_mem_len[b] < 0 || a->host_mem_len[b] > a->mem_cap)
           return fail(MSA_ERR_INVALID_ARG, "msa_route: host_mem_len[%d] = %d outside [0, mem_cap]", b,
                       a->host_mem_len[b]);
+    }
+    if (kernel_gather) {
+      const size_t row_bytes = 2 * (size_t)a->n_kv_heads * a->head_dim * elt_size(a->kv_dtype);
+      if (!aligned16(a->host_kv) || !aligned16(a->mem_kv) || row_bytes % 16 != 0)
+        return fail(MSA_ERR_INVALID_ARG, "msa_route: kernel assembly needs 16-byte aligned host_kv, mem_kv "
+                                         "and rows");
+      if (hipHostGetDevicePointer(&host_kv_dev, const_cast<void *>(a->host_kv), 0) != hipSuccess ||
+          !host_kv_dev) {
+        (void)hipGetLastError();
+        return fail(MSA_ERR_INVALID_ARG, "msa_route: host_kv is not device-mapped pinned memory");
+      }
     }
   }
 
@@ -163,11 +179,11 @@ int msa_route(const msa_route_args *a, void *stream) {
   RouteWs ws;
   route_ws_layout(a->dtype, a->batch, a->q_tokens, a->n_router_heads, a->router_dim, a->n_docs, a->n_pool,
                   a->top_k, a->workspace, &ws);
-  hipError_t e = launch_route(*a, ws, s);
+  hipError_t e = launch_route(*a, ws, host_kv_dev, s);
   if (e != hipSuccess) return hip_fail(e, "msa_route launch");
-  if (!assemble) return MSA_OK;
+  if (!assemble || kernel_gather) return MSA_OK;
 
-  // ---- context assembly: indices to the host, then one copy per document ----
+  // ---- host-driven assembly: indices to the host, then one copy per document ----
   ThreadEvents *ev = nullptr;
   if ((e = thread_events(&ev)) != hipSuccess) return hip_fail(e, "msa_route events");
   const size_t idx_bytes = sizeof(int32_t) * (size_t)a->batch * a->top_k;

@@ -105,16 +105,26 @@ const DeviceInfo &device_info();
 
 hipError_t launch_pool(const msa_pool_args &a, hipStream_t s);
 
+// One document's copy in the device-side context assembly.
+struct GatherPlan {
+  int64_t src_row;         // first pooled row in the host tier
+  int32_t rows;            // 0: nothing to copy (dropped or empty)
+  int32_t dst_row;         // first row in mem_kv[b]
+};
+
 struct RouteWs {  // carved out of the caller's workspace
-  float *row_score;        // [B, n_pool]
-  void *qprep;             // narrow: A fragments (bf16); valu: unit queries (fp32)
+  float *row_score;        // [n_pool, B]
+  float *qhat;             // [B*Tq, Hr*dr] fp32 unit queries (VALU scan only)
   uint64_t *cand;          // [B, n_blocks, cand_per_block]
+  GatherPlan *plan;        // [B, k]
   int32_t n_blocks;        // document blocks of the partial top-k
   int32_t cand_per_block;
 };
 size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t hr, int32_t dr,
                        int32_t n_docs, int64_t n_pool, int32_t top_k, void *base, RouteWs *ws);
-hipError_t launch_route(const msa_route_args &a, const RouteWs &ws, hipStream_t s);
+// host_kv_dev: device address of the pinned host tier for device-side
+// assembly, or NULL (no assembly, or host-driven copies)
+hipError_t launch_route(const msa_route_args &a, const RouteWs &ws, const void *host_kv_dev, hipStream_t s);
 
 size_t decode_ws_layout(int32_t batch, int32_t hq, int32_t d, int32_t mem_cap, int32_t local_cap,
                         void *base, float **part_acc, float **part_ml, int32_t *n_split);
