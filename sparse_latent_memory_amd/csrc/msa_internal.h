@@ -113,8 +113,9 @@ struct GatherPlan {
 };
 
 struct RouteWs {  // carved out of the caller's workspace
-  float *row_score;        // [n_pool, B]
-  float *qhat;             // [B*Tq, Hr*dr] fp32 unit queries (VALU scan only)
+  float *row_score;        // [B, n_pool]
+  float *qhat;             // [B*Tq, Hr*dr] fp32 unit queries (VALU and wide scans)
+  u32x4 *wide_frag;        // [n_mt, Hr*dr/32, 64] bf16 query fragments (wide scan)
   uint64_t *cand;          // [B, n_blocks, cand_per_block]
   GatherPlan *plan;        // [B, k]
   int32_t n_blocks;        // document blocks of the partial top-k

@@ -18,8 +18,7 @@
 //              norm per head, so no cross-lane reduction runs on the VALU.
 //              Otherwise (fp32, or more tokens) a prep kernel writes fp32
 //              unit queries and the scan is a per-row wave reduction.
-//              Output: row_score[j, b] = max over query b's tokens (row-major
-//              by bank row, so a row's B scores are one contiguous write).
+//              Output: row_score[b, j] = max over query b's tokens.
 //  2. block    per 256-document block: per-document max -> doc_scores, block
 //              top-k by a bitonic sort in LDS -> candidates.
 //  3. final    one workgroup per query selects the exact top-k: the k-th
@@ -44,6 +43,7 @@ constexpr int kDocsPerBlock = 256;
 constexpr int kWaves = 4;            // waves per workgroup in the scan / top-k kernels
 constexpr int kSortCap = kMaxTopK;   // keys the final selection can sort in LDS
 constexpr int kFastTopK = 64;        // k up to this uses the block-maximum bound (<= k*k survivors)
+constexpr int kWideChains = 1;       // query tiles in flight per wave in the wide scan (4 measured no faster)
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -223,14 +223,189 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
           for (int q = 1; q < 8; ++q) v = slot == q ? ts[q] : v;
           m = fmaxf(m, v);
         }
-        row_score[row * B + b] = m;
+        row_score[(int64_t)b * n_pool + row] = m;
       }
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// 1c. VALU scan (fp32, or bf16 with many query tokens): one wave per row
+// 1c. bf16 MFMA scan for many query tokens (more than 8)
+// --------------------------------------------------------------------------
+// The query side is laid out in M-tiles of 16 rows (one bf16-rounded unit
+// query token per row).  With one token per query (Tq == 1) a tile holds 16
+// queries.  Otherwise every query gets ceil(Tq/16) tiles of its own and the
+// rows past its last token repeat that token, which leaves the max over
+// tokens unchanged.  wide_frag[mt][f][lane] is fragment f = h*KS + s of tile
+// mt in the lane layout of the narrow scan.
+__global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict__ qhat, u32x4 *__restrict__ frag,
+                                                        int B, int Tq, int Hr, int dr, int n_mt) {
+  const int KS = dr / 32, NF = Hr * KS;
+  const int mtq = (Tq + 15) / 16;
+  const int64_t n = (int64_t)n_mt * NF * 64;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(idx & 63);
+    const int f = (int)((idx >> 6) % NF);
+    const int mt = (int)((idx >> 6) / NF);
+    const int h = f / KS, s = f % KS, r = l & 15;
+    int m = -1;                               // query token of this row, or none
+    if (Tq == 1) {
+      const int b = mt * 16 + r;
+      if (b < B) m = b;
+    } else {
+      const int b = mt / mtq;
+      const int t = min((mt % mtq) * 16 + r, Tq - 1);
+      m = b * Tq + t;
+    }
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (m >= 0) {
+      const float *src = qhat + ((int64_t)m * Hr + h) * dr + 32 * s + 8 * (l >> 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e >> 1] |= (uint32_t)f32_to_bf16(src[e]) << (16 * (e & 1));
+    }
+    u32x4 o;
+    o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
+    frag[idx] = o;
+  }
+}
+
+// One workgroup per CU, one wave per SIMD.  Each wave owns one 16-row bank
+// tile at a time with every head's fragments in registers, and loads the
+// next tile's while it computes: per head, 4 MFMAs give the tile's Gram
+// matrix (norms on its diagonal), then every query M-tile takes 4 MFMAs per
+// head against A-fragments read from LDS, scaled by the head's inverse norm.
+// Query tiles are staged into LDS MG at a time; when they do not all fit the
+// workgroup restages them per group of 4 bank tiles (barriers are uniform:
+// every wave walks the same number of groups).
+template <int HR, int KS>
+struct WideCfg {
+  static constexpr int NF = HR * KS;
+  static constexpr int MG = (128 / NF) < 16 ? (128 / NF) : 16;   // 128 KiB of query fragments
+};
+
+template <int HR, int KS>
+__global__ __launch_bounds__(256, 1) void scan_wide_kernel(const uint16_t *__restrict__ kr,
+                                                           const u32x4 *__restrict__ frag,
+                                                           float *__restrict__ row_score, int64_t n_pool, int B,
+                                                           int Tq, int n_mt) {
+  constexpr int NF = WideCfg<HR, KS>::NF;
+  constexpr int MG = WideCfg<HR, KS>::MG;
+  constexpr int ROW = NF * 32;
+  __shared__ u32x4 afrag[MG * NF * 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int diag_src = ((col >> 2) << 4) + col;
+  const int64_t n_tiles = (n_pool + 15) >> 4;
+  const int64_t n_groups = (n_tiles + kWaves - 1) / kWaves;
+  const int n_chunks = (n_mt + MG - 1) / MG;
+  const int mtq = (Tq + 15) / 16;
+
+  auto stage = [&](int c) {
+    const int mt0 = c * MG, nm = min(MG, n_mt - mt0);
+    const u32x4 *src = frag + (int64_t)mt0 * NF * 64;
+    for (int i = threadIdx.x; i < nm * NF * 64; i += blockDim.x) afrag[i] = src[i];
+  };
+  if (n_chunks == 1) stage(0);
+  __syncthreads();
+
+  auto load_tile = [&](int64_t grp_idx, u32x4 *dst) {
+    const int64_t tile = grp_idx * kWaves + wave;
+    int64_t row = tile * 16 + col;
+    row = row < n_pool ? row : n_pool - 1;
+    const uint16_t *rp = kr + row * ROW + 8 * grp;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) dst[f] = ld16(rp + 32 * f);
+  };
+
+  u32x4 cur[NF], nxt[NF];
+  int64_t gi = blockIdx.x;
+  if (gi < n_groups) load_tile(gi, cur);
+  for (; gi < n_groups; gi += gridDim.x) {
+    const int64_t gnext = gi + gridDim.x;
+    if (gnext < n_groups) load_tile(gnext, nxt);
+    const int64_t tile = gi * kWaves + wave;
+    const int64_t row = tile * 16 + col;
+
+    float inv[HR];
+#pragma unroll
+    for (int h = 0; h < HR; ++h) {
+      f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, cur[h * KS + s]);
+        g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, bv, g, 0, 0, 0);
+      }
+      const int di = col & 3;
+      const float mine = di == 0 ? g[0] : di == 1 ? g[1] : di == 2 ? g[2] : g[3];
+      inv[h] = rsqrtf(fmaxf(__shfl(mine, diag_src, 64), kEps2));
+    }
+
+    float qmax = -INFINITY;      // running max over the tiles of one query (Tq > 1)
+    for (int c = 0; c < n_chunks; ++c) {
+      if (n_chunks > 1) {
+        __syncthreads();
+        stage(c);
+        __syncthreads();
+      }
+      const int nm = min(MG, n_mt - c * MG);
+      // four query tiles at a time: four independent MFMA accumulation chains
+      for (int mi0 = 0; mi0 < nm; mi0 += kWideChains) {
+        f32x4 acc[kWideChains];
+#pragma unroll
+        for (int u = 0; u < kWideChains; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < HR; ++h) {
+          f32x4 d[kWideChains];
+#pragma unroll
+          for (int u = 0; u < kWideChains; ++u) d[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, cur[h * KS + s]);
+#pragma unroll
+            for (int u = 0; u < kWideChains; ++u) {
+              // slots past the staged tiles hold stale fragments; their results are discarded
+              const int mi = min(mi0 + u, MG - 1);
+              const bf16x8 av = __builtin_bit_cast(bf16x8, afrag[(mi * NF + h * KS + s) * 64 + lane]);
+              d[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, d[u], 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kWideChains; ++u) acc[u] += d[u] * inv[h];
+        }
+#pragma unroll
+        for (int u = 0; u < kWideChains; ++u) {
+          if (mi0 + u >= nm) break;
+          const int mt = c * MG + mi0 + u;
+          if (Tq == 1) {
+            // rows 4*grp + i of this tile are queries mt*16 + 4*grp + i
+            if (row < n_pool) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int b = mt * 16 + 4 * grp + i;
+                if (b < B) row_score[(int64_t)b * n_pool + row] = acc[u][i];
+              }
+            }
+          } else {
+            float m = fmaxf(fmaxf(acc[u][0], acc[u][1]), fmaxf(acc[u][2], acc[u][3]));
+            m = fmaxf(m, __shfl_xor(m, 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            qmax = fmaxf(qmax, m);
+            if (mt % mtq == mtq - 1) {
+              if (grp == 0 && row < n_pool) row_score[(int64_t)(mt / mtq) * n_pool + row] = qmax;
+              qmax = -INFINITY;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) cur[f] = nxt[f];
+  }
+}
+
+// --------------------------------------------------------------------------
+// 1d. VALU scan (fp32): one wave per row
 // --------------------------------------------------------------------------
 template <typename T, int EPL>
 __global__ __launch_bounds__(256) void scan_valu_kernel(const T *__restrict__ kr, const float *__restrict__ qhat,
@@ -259,7 +434,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T *__restrict__ kr
         for (int e = 0; e < EPL; ++e) p += q[e] * x[e];
         best = fmaxf(best, wave_sum(p));
       }
-      if (lane == 0) row_score[row * B + b] = best;
+      if (lane == 0) row_score[(int64_t)b * n_pool + row] = best;
     }
   }
 }
@@ -300,15 +475,14 @@ __global__ __launch_bounds__(kDocsPerBlock) void doc_block_topk_kernel(
     int64_t r0 = pool_off[d], r1 = pool_off[d + 1];
     r0 = max((int64_t)0, min(r0, n_pool));
     r1 = max(r0, min(r1, n_pool));
-    const int B = gridDim.y;
-    const float *rs = row_score + b;
+    const float *rs = row_score + (int64_t)b * n_pool;
     float best = -INFINITY;
     int64_t r = r0;
     for (; r + 4 <= r1; r += 4) {      // independent loads in flight
-      const float x0 = rs[r * B], x1 = rs[(r + 1) * B], x2 = rs[(r + 2) * B], x3 = rs[(r + 3) * B];
+      const float x0 = rs[r], x1 = rs[r + 1], x2 = rs[r + 2], x3 = rs[r + 3];
       best = fmaxf(best, fmaxf(fmaxf(x0, x1), fmaxf(x2, x3)));
     }
-    for (; r < r1; ++r) best = fmaxf(best, rs[r * B]);
+    for (; r < r1; ++r) best = fmaxf(best, rs[r]);
     doc_scores[(int64_t)b * n_docs + d] = best;
     kk = doc_key(best, d);
   }
@@ -486,10 +660,30 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
 // --------------------------------------------------------------------------
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool mfma_path(int32_t dtype, int32_t M, int32_t hr, int32_t dr) {
-  if (dtype != MSA_BF16 || M > 8) return false;
+bool mfma_shape(int32_t hr, int32_t dr) {
   const int ks = dr / 32;
   return (ks == 2 || ks == 4) && (hr == 1 || hr == 2 || hr == 4 || hr == 8 || (hr == 16 && ks == 2));
+}
+// bf16, at most 8 query tokens: fused-prep scan with hi/lo query rows
+bool mfma_path(int32_t dtype, int32_t M, int32_t hr, int32_t dr) {
+  return dtype == MSA_BF16 && M <= 8 && mfma_shape(hr, dr);
+}
+// bf16, more query tokens: query M-tiles streamed through LDS
+bool wide_path(int32_t dtype, int32_t M, int32_t hr, int32_t dr) {
+  return dtype == MSA_BF16 && M > 8 && mfma_shape(hr, dr);
+}
+int wide_tiles(int32_t batch, int32_t q_tokens) {
+  return q_tokens == 1 ? (batch + 15) / 16 : batch * ((q_tokens + 15) / 16);
+}
+
+template <int HR, int KS>
+hipError_t launch_scan_wide(const msa_route_args &a, const RouteWs &ws, hipStream_t s) {
+  const int64_t n_groups = ((a.n_pool + 15) / 16 + kWaves - 1) / kWaves;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(device_info().n_cu, n_groups));
+  hipLaunchKernelGGL((scan_wide_kernel<HR, KS>), dim3(grid), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t *>(a.kr_pooled), ws.wide_frag, ws.row_score, a.n_pool,
+                     a.batch, a.q_tokens, wide_tiles(a.batch, a.q_tokens));
+  return hipGetLastError();
 }
 
 template <int HR, int KS>
@@ -553,6 +747,9 @@ size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t h
   off = align256(off + sizeof(float) * (size_t)batch * (size_t)n_pool);
   const size_t o_q = off;
   if (!mfma_path(dtype, M, hr, dr)) off = align256(off + sizeof(float) * (size_t)M * hr * dr);
+  const size_t o_w = off;
+  if (wide_path(dtype, M, hr, dr))
+    off = align256(off + sizeof(u32x4) * 64 * (size_t)hr * (dr / 32) * wide_tiles(batch, q_tokens));
   const size_t o_c = off;
   off = align256(off + sizeof(uint64_t) * (size_t)batch * n_blocks * cpb);
   const size_t o_plan = off;
@@ -561,6 +758,7 @@ size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t h
     char *p = reinterpret_cast<char *>(base);
     ws->row_score = reinterpret_cast<float *>(p + o_rs);
     ws->qhat = reinterpret_cast<float *>(p + o_q);
+    ws->wide_frag = reinterpret_cast<u32x4 *>(p + o_w);
     ws->cand = reinterpret_cast<uint64_t *>(p + o_c);
     ws->plan = reinterpret_cast<GatherPlan *>(p + o_plan);
     ws->n_blocks = n_blocks;
@@ -600,8 +798,29 @@ hipError_t launch_route(const msa_route_args &a, const RouteWs &ws, const void *
       hipLaunchKernelGGL(prep_unit_kernel<float>, dim3(grid), dim3(256), 0, s,
                          reinterpret_cast<const float *>(a.qr), ws.qhat, M, a.n_router_heads, a.router_dim);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
-    e = bf16 ? launch_scan_valu<uint16_t>(a, ws, s) : launch_scan_valu<float>(a, ws, s);
+    if (wide_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
+      const int n_mt = wide_tiles(a.batch, a.q_tokens);
+      const int64_t n = (int64_t)n_mt * a.n_router_heads * (a.router_dim / 32) * 64;
+      hipLaunchKernelGGL(prep_wide_kernel, dim3((int)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s,
+                         ws.qhat, ws.wide_frag, a.batch, a.q_tokens, a.n_router_heads, a.router_dim, n_mt);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+      switch (a.n_router_heads * 8 + a.router_dim / 32) {
+        case 1 * 8 + 2: e = launch_scan_wide<1, 2>(a, ws, s); break;
+        case 1 * 8 + 4: e = launch_scan_wide<1, 4>(a, ws, s); break;
+        case 2 * 8 + 2: e = launch_scan_wide<2, 2>(a, ws, s); break;
+        case 2 * 8 + 4: e = launch_scan_wide<2, 4>(a, ws, s); break;
+        case 4 * 8 + 2: e = launch_scan_wide<4, 2>(a, ws, s); break;
+        case 4 * 8 + 4: e = launch_scan_wide<4, 4>(a, ws, s); break;
+        case 8 * 8 + 2: e = launch_scan_wide<8, 2>(a, ws, s); break;
+        case 8 * 8 + 4: e = launch_scan_wide<8, 4>(a, ws, s); break;
+        case 16 * 8 + 2: e = launch_scan_wide<16, 2>(a, ws, s); break;
+        default: e = hipErrorInvalidValue;
+      }
+    } else {
+      if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+      e = bf16 ? launch_scan_valu<uint16_t>(a, ws, s) : launch_scan_valu<float>(a, ws, s);
+    }
   }
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;

@@ -161,14 +161,50 @@ def test_route_matrix_core_path(hr, dr, b, tq):
     _route_check(kr, off, qr, 16, f"mfma {hr}x{dr} B{b} Tq{tq}")
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("b,tq", [(1, 16), (4, 3), (9, 1)])
-def test_route_vector_path(dtype, b, tq):
+def test_route_vector_path_fp32(b, tq):
     g = torch.Generator().manual_seed(b * 31 + tq)
-    kr, off = _ragged_bank(g, 500, 4, 8, 128, dtype)
-    qr = _randn(g, b, tq, 8, 128, dtype=dtype).to(DEV)
-    _say(f"route: vector path B={b} Tq={tq} {dtype}")
+    kr, off = _ragged_bank(g, 500, 4, 8, 128, torch.float32)
+    qr = _randn(g, b, tq, 8, 128).to(DEV)
+    _say(f"route: fp32 vector path B={b} Tq={tq}")
     _route_check(kr, off, qr, 8, f"valu B{b} Tq{tq}")
+
+
+@pytest.mark.parametrize("hr,dr", [(8, 128), (4, 64), (16, 64), (1, 128)])
+@pytest.mark.parametrize("b,tq", [(1, 16), (4, 3), (9, 1), (20, 1), (3, 40), (100, 1), (1, 256)])
+def test_route_many_tokens_matrix_core_path(hr, dr, b, tq):
+    """More than 8 query tokens: bf16 query M-tiles through LDS (restaged
+    when they exceed one LDS load), tokens of a query padded to whole tiles."""
+    g = torch.Generator().manual_seed(hr * 1000 + dr + b * 7 + tq)
+    kr, off = _ragged_bank(g, 600, 4, hr, dr, torch.bfloat16)
+    qr = _randn(g, b, tq, hr, dr, dtype=torch.bfloat16).to(DEV)
+    _say(f"route: wide MFMA path Hr={hr} dr={dr} B={b} Tq={tq} rows={off[-1]}")
+    _route_check(kr, off, qr, 8, f"wide {hr}x{dr} B{b} Tq{tq}")
+
+
+def test_route_prefill_config_full_size():
+    """Routing layer of a 4B-parameter backbone: 2048 documents (lengths
+    U[256,1024], ~21.8K pooled rows), a 256-token query prefill, top-16;
+    every document score checked against the oracle."""
+    cfg = synth.config(2)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    _say(f"route: prefill routing, {len(lens)} docs, {off[-1]} rows, Tq=256")
+    kr = synth.pooled_router_bank(cfg, lens, device=DEV)
+    qr = synth.router_queries(cfg, device=DEV)
+    _route_check(kr, off, qr, cfg.top_k, "prefill 256")
+
+
+def test_route_interleave_batch_shape():
+    """64 queries of one token against a ragged lognormal bank (the
+    multi-hop workload's routing shape, smaller bank)."""
+    cfg = synth.config(5, total_tokens=3_000_000)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    _say(f"route: 64 queries, {len(lens)} docs, {off[-1]} rows")
+    kr = synth.pooled_router_bank(cfg, lens, device=DEV)
+    qr = synth.router_queries(cfg, device=DEV)
+    _route_check(kr, off, qr, cfg.top_k, "64 queries")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
