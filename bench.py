@@ -35,15 +35,19 @@ import sparse_latent_memory_amd as msa  # noqa: E402
 from sparse_latent_memory_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E peak, GB/s
-SCAN_SOURCE = os.path.join(ROOT, "sparse_latent_memory_amd", "csrc", "route.hip")
+# the measured scan kernel's own source and the device helpers it includes
+SCAN_SOURCES = [os.path.join(ROOT, "sparse_latent_memory_amd", "csrc", f) for f in ("route_scan.hip", "msa_device.h")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "route_scan_100M_bank.traffic.json")
 CALIBRATION_BYTES = 1 << 30
 
 
-def source_digest(path):
+def source_digest(paths):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
@@ -55,7 +59,7 @@ def measured_traffic():
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_digest(SCAN_SOURCE):
+    if rec.get("source_sha256") != source_digest(SCAN_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -71,6 +75,60 @@ def calibrate_copy():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"calibration_copy_bytes": CALIBRATION_BYTES, "launches": 3}), flush=True)
+
+
+SCAN_KERNEL = "scan_mfma_kernel<8, 4, 1>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_kib(run_dir, counter, kernel):
+    """Average KiB per dispatch of one rocprofv3 --pmc counter over the
+    dispatches of `kernel` (and how many there were), from the
+    run_counter_collection.csv under run_dir."""
+    import csv
+    import glob
+    per_dispatch = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]:
+                    key = (path, r["Dispatch_Id"])
+                    per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    if not per_dispatch:
+        raise SystemExit(f"no {counter} values for {kernel} under {run_dir}")
+    return sum(per_dispatch.values()) / len(per_dispatch), len(per_dispatch)
+
+
+def write_traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """HBM bytes per scan launch from FETCH_SIZE / WRITE_SIZE counter runs of
+    this bench and of --calibrate-copy, each counter scaled by what it reads
+    for the 1 GiB copy (which moves exactly that many bytes each way)."""
+    cfg = synth.config(4)
+    n_pool = int(synth.row_offsets(synth.doc_lengths(cfg), cfg.pool)[-1])
+    fetch, n = _counter_kib(fetch_dir, "FETCH_SIZE", SCAN_KERNEL)
+    write, _ = _counter_kib(write_dir, "WRITE_SIZE", SCAN_KERNEL)
+    cfetch, _ = _counter_kib(copy_fetch_dir, "FETCH_SIZE", COPY_KERNEL)
+    cwrite, _ = _counter_kib(copy_write_dir, "WRITE_SIZE", COPY_KERNEL)
+    fscale = CALIBRATION_BYTES / (cfetch * 1024)
+    wscale = CALIBRATION_BYTES / (cwrite * 1024)
+    hbm = fetch * 1024 * fscale + write * 1024 * wscale
+    algo = n_pool * cfg.n_router_heads * cfg.router_dim * 2 + cfg.n_router_heads * cfg.router_dim * 2
+    rec = {
+        "kernel": f"msa::{SCAN_KERNEL} (route bank scan, 100M-token bank, 1 query token)",
+        "sources": [os.path.relpath(p, ROOT) for p in SCAN_SOURCES],
+        "source_sha256": source_digest(SCAN_SOURCES),
+        "fetch_kib_per_launch_raw": fetch,
+        "write_kib_per_launch_raw": write,
+        "launches": n,
+        "copy_calibration": {"bytes": CALIBRATION_BYTES, "kernel": COPY_KERNEL, "fetch_kib_raw": cfetch,
+                             "write_kib_raw": cwrite, "fetch_scale": fscale, "write_scale": wscale},
+        "hbm_bytes_per_launch": hbm,
+        "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": hbm / algo,
+    }
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 class HipEvents:
@@ -108,11 +166,18 @@ def main():
     ap.add_argument("--latency-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--write-traffic-record", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the scan's HBM traffic record from four rocprofv3 --pmc output folders "
+                         "(this bench with FETCH_SIZE, with WRITE_SIZE; --calibrate-copy with each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.write_traffic_record:
+        write_traffic_record(*args.write_traffic_record)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the bank is held whole in one GPU's HBM); "
@@ -246,7 +311,7 @@ def main():
             "global_batch": cfg.batch,
         },
         "roofline": {
-            "kernel": "route bank scan (scan_mfma_kernel<8,4>)",
+            "kernel": f"route bank scan ({SCAN_KERNEL})",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -112,12 +112,15 @@ int msa_pool_encode(const msa_pool_args *args, void *stream);
  *   Dsc[b,d]  = max over t and over the rows j of document d of s[b,t,j]
  *   top-k     = the k documents with the largest Dsc[b,.], ties to the
  *               lower document id, in that order.
- * Sources: as for stage 1 ("cosine similarity, mean-pooled across heads and
- * then maxed over tokens, picks the Top-k documents" is restated there).
+ * Sources: as for stage 1, whose routing paragraph defines the score as a
+ * cosine averaged over router heads, then its maximum over tokens, and the
+ * selection as the k best documents.
  * doc_scores is always written.  Arithmetic: bf16 inputs are multiplied in
- * the matrix cores with fp32 accumulation (the normalised query is split
- * into two bf16 terms when at most 8 query tokens are routed at once);
- * fp32 inputs use fp32 vector arithmetic.
+ * the matrix cores with fp32 accumulation.  With at most 8 query tokens in
+ * the call the normalised query is split into two bf16 terms (about 16
+ * mantissa bits); with more it is rounded once to bf16 (relative error at
+ * most 2^-9 per element, so a score moves by at most ~2e-3 and in practice
+ * by ~1e-5).  fp32 inputs use fp32 vector arithmetic.
  *
  * Assembly (when host_kv != NULL): the selected documents' pooled rows
  * host_kv[doc_pool_off[d] .. doc_pool_off[d+1]) are copied, in rank order,

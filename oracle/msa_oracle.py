@@ -12,8 +12,8 @@ titles [HL], [TM], [GF]):
 2. Online routing: the projected query Qr is compared with every pooled
    router key by cosine similarity, averaged over router heads, maximised
    over tokens, and the top-k documents are selected ([HL], [TM] stage 2).
-3. Context assembly: the selected documents' pooled K/V are concatenated
-   with the query's local K/V ([HL]; [TM] stage 2).
+3. Context assembly: the pooled K/V of the chosen documents, in rank
+   order, followed by the query's own K/V ([HL]; [TM] stage 2).
 4. Sparse generation: attention over that assembled context, with the
    query's start position offset by k, the number of retrieved documents,
    keeping the order background -> query -> generation ([HL]; [TM] stage 3).
@@ -26,8 +26,8 @@ Readings where the pages are silent (each is also listed in the design doc):
   position, then averaged); V and Kr are not rotated.
 * R3 RoPE is the rotate-half form with inverse frequencies
   theta^(-2j/D), j < D/2.
-* R4 "maxed over tokens" covers the query tokens and the pooled rows of a
-  document (max of max, so both readings agree).
+* R4 the maximum over tokens covers the query tokens and the pooled rows
+  of a document (max of max, so both readings agree).
 * R5 cosine uses max(||x||, 1e-8) per vector.
 * R6 top-k orders by score descending, then document id ascending.
 * R7 assembled memory = the selected documents' pooled rows in rank order;

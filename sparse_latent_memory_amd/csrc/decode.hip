@@ -2,9 +2,9 @@
 //
 // Method: "EverMind-AI/MSA: Memory Sparse Attention for 100M-Token Contexts"
 // (hysenlabs.com), section "How MSA compresses and routes documents" (the
-// selected documents' compressed K/V are concatenated with the query's local
-// K/V; global RoPE offsets the query start by k, order background -> query ->
-// generation) and stage 3 of "EverMind Releases Memory-Sparse Attention Code
+// pooled K/V of the chosen documents come first and the query's own K/V
+// after them; global RoPE moves the query start by k, keeping the order
+// background -> query -> generation) and stage 3 of "EverMind Releases Memory-Sparse Attention Code
 // for Long-Context AI Models" (toolmesh.ai), "Architectural Design and
 // Inference".
 //
@@ -38,12 +38,6 @@ __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256, 3) void decode_split_kernel(
     const T *__restrict__ q, const T *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,

@@ -5,95 +5,9 @@
 #include <stdint.h>
 
 #include "../../include/msa.h"
+#include "msa_device.h"
 
 namespace msa {
-
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
-
-constexpr float kEps = 1e-8f;          // cosine norm clamp
-constexpr float kEps2 = 1e-16f;        // kEps squared (clamp on squared norms)
-constexpr int kMaxTopK = 4096;
-
-// ---------------------------------------------------------------------------
-// bf16 <-> fp32.  Storage is raw uint16_t; bf16 is the top half of an fp32.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// round to nearest, ties to even (finite inputs; NaN stays NaN)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// Element access templated on the storage type: float or uint16_t (bf16).
-template <typename T> struct Elt;
-template <> struct Elt<float> {
-  static constexpr int kPerVec = 4;  // elements per 16-byte vector
-  __device__ static __forceinline__ float get(const float *p, int64_t i) { return p[i]; }
-  __device__ static __forceinline__ void put(float *p, int64_t i, float x) { p[i] = x; }
-  __device__ static __forceinline__ void unpack(const u32x4 &v, float *o) {
-    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
-    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
-  }
-  __device__ static __forceinline__ u32x4 pack(const float *o) {
-    u32x4 v; v.x = __float_as_uint(o[0]); v.y = __float_as_uint(o[1]);
-    v.z = __float_as_uint(o[2]); v.w = __float_as_uint(o[3]);
-    return v;
-  }
-};
-template <> struct Elt<uint16_t> {
-  static constexpr int kPerVec = 8;
-  __device__ static __forceinline__ float get(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
-  __device__ static __forceinline__ void put(uint16_t *p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
-  __device__ static __forceinline__ void unpack(const u32x4 &v, float *o) {
-    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
-    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
-  }
-  __device__ static __forceinline__ u32x4 pack(const float *o) {
-    u32x4 v;
-    v.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-    v.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-    v.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
-    v.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
-    return v;
-  }
-};
-
-__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
-__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-__device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
-
-// Accurate (cos, sin) of pos * omega for a large integer position: the angle
-// is formed in fp64 in revolutions (omega / 2pi), its integer part dropped
-// exactly, and the remaining half-revolution fraction evaluated with fp32
-// sincospi, whose argument reduction is exact (no large-argument path).
-__device__ __forceinline__ void rope_phasor_rev(double pos, double rev_per_pos, float *c, float *s) {
-  double r = pos * rev_per_pos;
-  r -= rint(r);                               // |r| <= 1/2 revolution
-  sincospif((float)(2.0 * r), s, c);
-}
-__device__ __forceinline__ void rope_phasor(double pos, double omega, float *c, float *s) {
-  rope_phasor_rev(pos, omega * 0.15915494309189533577, c, s);
-}
-
-// Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
-// -0 and +0 map to the same key.
-__device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_score(uint32_t k) {
-  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-  return __uint_as_float(u);
-}
 
 // ---------------------------------------------------------------------------
 // launchers (validated arguments only)
@@ -113,14 +27,95 @@ struct GatherPlan {
 };
 
 struct RouteWs {  // carved out of the caller's workspace
-  float *row_score;        // [B, n_pool]
+  float *row_score;        // [B, n_parts, n_pool]
   float *qhat;             // [B*Tq, Hr*dr] fp32 unit queries (VALU and wide scans)
   u32x4 *wide_frag;        // [n_mt, Hr*dr/32, 64] bf16 query fragments (wide scan)
   uint64_t *cand;          // [B, n_blocks, cand_per_block]
   GatherPlan *plan;        // [B, k]
   int32_t n_blocks;        // document blocks of the partial top-k
   int32_t cand_per_block;
+  int32_t n_parts;         // partial token maxima per query in row_score (wide scan), else 1
 };
+// Routing kernels.  The bank scan writes row_score[b, j] (max over query b's
+// tokens of the head-mean cosine); selection reduces it per document, takes
+// the exact top-k and plans/performs the device-side assembly.
+constexpr int kDocsPerBlock = 256;    // documents per partial top-k block
+
+// v_mfma_f32_16x16x32_bf16 scan shapes: router dim 64 or 128, heads a power
+// of two up to 8 (16 with dim 64)
+inline bool mfma_shape(int32_t hr, int32_t dr) {
+  const int ks = dr / 32;
+  return (ks == 2 || ks == 4) && (hr == 1 || hr == 2 || hr == 4 || hr == 8 || (hr == 16 && ks == 2));
+}
+// query M-tiles of 16 rows in the wide scan
+__host__ __device__ inline int wide_tiles(int32_t batch, int32_t q_tokens) {
+  return q_tokens == 1 ? (batch + 15) / 16 : batch * ((q_tokens + 15) / 16);
+}
+// Query M-tiles the wide scan keeps in LDS at once, for ks = dr/32
+// fragments per head and nf = Hr*ks per tile: at most 128 KiB of bf16
+// fragments, at most 8 tiles, and at most 16/ks tiles, so one head's query
+// fragments (NM*ks*4 registers) fit beside the accumulators at two waves
+// per SIMD.
+__host__ __device__ constexpr int wide_mg(int nf, int ks) {
+  return (128 / nf < 16 / ks ? 128 / nf : 16 / ks) < 8 ? (128 / nf < 16 / ks ? 128 / nf : 16 / ks) : 8;
+}
+// How the wide scan splits the query tiles into chunks of at most mg tiles.
+// Tq == 1: a tile holds 16 queries; chunk c = tiles [c*mg, (c+1)*mg).
+// Tq > 1: query b owns mtq = ceil(Tq/16) tiles.  If mtq <= mg a chunk holds
+// qpc = mg/mtq whole queries; otherwise query b is cut into ppq parts of at
+// most mg tiles, each scanned by its own workgroup, and row_score gets one
+// partial max per part: row_score[(b*n_parts + part)*n_pool + j].
+struct WideLayout {
+  int tok1;        // Tq == 1
+  int mg, mtq, n_mt, qpc, ppq, n_chunks, n_parts;
+};
+__host__ __device__ inline WideLayout wide_layout(int32_t batch, int32_t q_tokens, int mg) {
+  WideLayout L;
+  L.mg = mg;
+  L.tok1 = q_tokens == 1;
+  L.n_mt = wide_tiles(batch, q_tokens);
+  if (L.tok1) {
+    L.mtq = 1; L.qpc = 16; L.ppq = 1;
+    L.n_chunks = (L.n_mt + mg - 1) / mg;
+  } else {
+    L.mtq = (q_tokens + 15) / 16;
+    if (L.mtq <= mg) {
+      L.qpc = mg / L.mtq; L.ppq = 1;
+      L.n_chunks = (batch + L.qpc - 1) / L.qpc;
+    } else {
+      L.qpc = 0; L.ppq = (L.mtq + mg - 1) / mg;
+      L.n_chunks = batch * L.ppq;
+    }
+  }
+  L.n_parts = L.ppq;
+  return L;
+}
+// tiles [t0, t1) of chunk c
+__host__ __device__ inline void wide_chunk(const WideLayout &L, int c, int *t0, int *t1) {
+  if (L.tok1) {
+    *t0 = c * L.mg;
+    *t1 = c * L.mg + L.mg < L.n_mt ? c * L.mg + L.mg : L.n_mt;
+  } else if (L.ppq == 1) {
+    *t0 = c * L.qpc * L.mtq;
+    *t1 = (c + 1) * L.qpc * L.mtq < L.n_mt ? (c + 1) * L.qpc * L.mtq : L.n_mt;
+  } else {
+    const int q = c / L.ppq, p = c % L.ppq;
+    *t0 = q * L.mtq + p * L.mg;
+    *t1 = q * L.mtq + ((p + 1) * L.mg < L.mtq ? (p + 1) * L.mg : L.mtq);
+  }
+}
+// bf16, at most 8 query tokens (route_scan.hip)
+hipError_t launch_scan_narrow(const msa_route_args &a, float *row_score, hipStream_t s);
+// fp32 unit queries (route_scan_wide.hip)
+hipError_t launch_prep_unit(const msa_route_args &a, float *qhat, hipStream_t s);
+// bf16 query fragments and the MFMA scan for more than 8 tokens
+hipError_t launch_prep_wide(const msa_route_args &a, const float *qhat, u32x4 *frag, hipStream_t s);
+hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s);
+// fp32 (any token count): one wave per bank row
+hipError_t launch_scan_valu(const msa_route_args &a, const float *qhat, float *row_score, hipStream_t s);
+// per-document max, exact top-k, assembly plan and device-side gather (route_select.hip)
+hipError_t launch_select(const msa_route_args &a, const RouteWs &ws, const void *host_kv_dev, hipStream_t s);
+
 size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t hr, int32_t dr,
                        int32_t n_docs, int64_t n_pool, int32_t top_k, void *base, RouteWs *ws);
 // host_kv_dev: device address of the pinned host tier for device-side

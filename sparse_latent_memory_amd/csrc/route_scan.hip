@@ -1,0 +1,218 @@
+// Routing, stage 2 of the method: the bank scan for at most 8 bf16 query
+// tokens (decode-time routing, one or a few queries).
+//
+// Method: "EverMind-AI/MSA: Memory Sparse Attention for 100M-Token Contexts"
+// (hysenlabs.com), section "How MSA compresses and routes documents": the
+// score of a pooled row is the cosine of the routing query and the pooled
+// router key, averaged over router heads and maximised over query tokens.
+//
+// The bank is streamed once from HBM, one 16-row tile per wave step.  Every
+// workgroup first builds the normalised query as MFMA A-fragments in LDS:
+// each token is split into a bf16 head and a bf16 remainder row, so the
+// query keeps ~16 mantissa bits.  v_mfma_f32_16x16x32_bf16 then computes the
+// query dot products and the 16x16 Gram matrix of the tile (A = B = bank
+// fragment), whose diagonal is every row's squared norm per head, so no
+// cross-lane reduction runs on the VALU.  Output: row_score[b, j] = max over
+// query b's tokens.
+#include "msa_internal.h"
+
+#include <algorithm>
+
+namespace msa {
+namespace {
+
+constexpr int kWaves = 4;   // waves per workgroup
+
+// --------------------------------------------------------------------------
+// bf16 MFMA scan with the query preparation fused in
+// --------------------------------------------------------------------------
+// A-fragment f = h*KS + s, lane l holds A[row = l%16][k = 32 s + 8 (l/16) + e]
+// (e < 8) of head h.  Row 2m is the bf16 rounding of unit query token m, row
+// 2m+1 the bf16 rounding of its remainder; rows of absent tokens are zero.
+// Lane l owns bank row (tile*16 + l%16) and the same k slice, so one load
+// instruction of the wave reads 16 rows x 64 contiguous bytes.  Heads are
+// loaded in groups of HG, one group ahead of the MFMAs that consume them.
+#ifndef MSA_SCAN_HG
+#define MSA_SCAN_HG 1
+#endif
+#ifndef MSA_SCAN_PIPE      // 1: keep the head-group loop rolled (fewer registers)
+#define MSA_SCAN_PIPE 0
+#endif
+#ifndef MSA_SCAN_NT        // 1: non-temporal bank loads (the bank is read once per call)
+#define MSA_SCAN_NT 0
+#endif
+#ifndef MSA_SCAN_CHUNKED   // 1: contiguous tile range per wave; 0: tiles strided over waves
+#define MSA_SCAN_CHUNKED 0
+#endif
+#ifndef MSA_SCAN_GRID_MULT // workgroups launched per resident workgroup slot
+#define MSA_SCAN_GRID_MULT 1
+#endif
+#if MSA_SCAN_NT
+#define SCAN_LD ld16_nt
+#else
+#define SCAN_LD ld16
+#endif
+
+template <int HR, int KS, int HG>
+__global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restrict__ kr,
+                                                        const uint16_t *__restrict__ qr,
+                                                        float *__restrict__ row_score, int64_t n_pool, int B,
+                                                        int Tq) {
+  constexpr int NF = HR * KS;                     // fragments per 16-row tile per lane
+  constexpr int DR = KS * 32;                     // router head dim
+  constexpr int ROW = HR * DR;                    // elements per bank row
+  constexpr int NG = HR / HG;                     // head groups per tile
+  constexpr int GF = HG * KS;                     // fragments per head group
+  __shared__ u32x4 afrag[NF * 64];
+  __shared__ float qscale[8 * HR];
+  const int M = B * Tq;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+  for (int mh = wave; mh < M * HR; mh += kWaves) {
+    const uint16_t *src = qr + (int64_t)mh * DR;
+    float ss = 0.f;
+    for (int i = lane; i < DR; i += 64) {
+      const float x = bf16_to_f32(src[i]);
+      ss += x * x;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) qscale[mh] = 1.0f / (fmaxf(sqrtf(ss), kEps) * (float)HR);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NF * 64; idx += blockDim.x) {
+    const int l = idx & 63, f = idx >> 6;
+    const int h = f / KS, s = f % KS;
+    const int r = l & 15, m = r >> 1;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (m < M) {
+      const uint16_t *src = qr + ((int64_t)m * HR + h) * DR + 32 * s + 8 * (l >> 4);
+      const float sc = qscale[m * HR + h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = bf16_to_f32(src[e]) * sc;
+        const uint16_t hi = f32_to_bf16(x);
+        const uint16_t val = (r & 1) ? f32_to_bf16(x - bf16_to_f32(hi)) : hi;
+        w[e >> 1] |= (uint32_t)val << (16 * (e & 1));
+      }
+    }
+    u32x4 o;
+    o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
+    afrag[idx] = o;
+  }
+  __syncthreads();
+
+  const int col = lane & 15, grp = lane >> 4;
+  const int diag_src = ((col >> 2) << 4) + col;    // lane holding Gram[col][col]
+  const int64_t n_tiles = (n_pool + 15) >> 4;
+
+#if MSA_SCAN_CHUNKED
+  // each wave streams one contiguous run of tiles
+  const int64_t n_waves = (int64_t)gridDim.x * kWaves, wid = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t t_begin = n_tiles * wid / n_waves, t_end = n_tiles * (wid + 1) / n_waves;
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
+#else
+  for (int64_t tile = (int64_t)blockIdx.x * kWaves + wave; tile < n_tiles;
+       tile += (int64_t)gridDim.x * kWaves) {
+#endif
+    const int64_t row = tile * 16 + col;
+    const int64_t rowc = row < n_pool ? row : n_pool - 1;
+    const uint16_t *rp = kr + rowc * ROW + 8 * grp;
+    u32x4 cur[GF];
+#pragma unroll
+    for (int f = 0; f < GF; ++f) cur[f] = SCAN_LD(rp + 32 * f);
+
+    float sc0 = 0.f, sc1 = 0.f;
+#if MSA_SCAN_PIPE
+#pragma unroll 1
+#else
+#pragma unroll
+#endif
+    for (int gi = 0; gi < NG; ++gi) {
+      u32x4 nxt[GF];
+      if (gi + 1 < NG) {
+#pragma unroll
+        for (int f = 0; f < GF; ++f) nxt[f] = SCAN_LD(rp + 32 * ((gi + 1) * GF + f));
+      }
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const int h = gi * HG + hh;
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, cur[hh * KS + s]);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, afrag[(h * KS + s) * 64 + lane]);
+          g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, bv, g, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, d, 0, 0, 0);
+        }
+        const int di = col & 3;
+        const float mine = di == 0 ? g[0] : di == 1 ? g[1] : di == 2 ? g[2] : g[3];
+        const float n2 = __shfl(mine, diag_src, 64);
+        const float inv = rsqrtf(fmaxf(n2, kEps2));
+        sc0 += (d[0] + d[1]) * inv;      // token 2*grp     (head + remainder rows)
+        sc1 += (d[2] + d[3]) * inv;      // token 2*grp + 1
+      }
+      if (gi + 1 < NG) {
+#pragma unroll
+        for (int f = 0; f < GF; ++f) cur[f] = nxt[f];
+      }
+    }
+    // gather the 8 token scores of column `col` into lanes 0..15
+    float ts[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ts[2 * q] = __shfl(sc0, col + 16 * q, 64);
+      ts[2 * q + 1] = __shfl(sc1, col + 16 * q, 64);
+    }
+    if (grp == 0 && row < n_pool) {
+      for (int b = 0; b < B; ++b) {
+        float m = -INFINITY;
+        for (int t = 0; t < Tq; ++t) {
+          const int slot = b * Tq + t;
+          float v = ts[0];
+#pragma unroll
+          for (int q = 1; q < 8; ++q) v = slot == q ? ts[q] : v;
+          m = fmaxf(m, v);
+        }
+        row_score[(int64_t)b * n_pool + row] = m;
+      }
+    }
+  }
+}
+
+template <int HR, int KS>
+hipError_t launch_scan_mfma(const msa_route_args &a, float *row_score, hipStream_t s) {
+  constexpr int HG = HR < MSA_SCAN_HG ? HR : MSA_SCAN_HG;
+  const int64_t n_tiles = (a.n_pool + 15) / 16;
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_mfma_kernel<HR, KS, HG>, 256, 0) != hipSuccess ||
+      occ < 1)
+    occ = 1;
+  const int64_t want = (int64_t)device_info().n_cu * occ * MSA_SCAN_GRID_MULT;
+  const int64_t need = (n_tiles + kWaves - 1) / kWaves;
+  const int grid = (int)std::max<int64_t>(1, std::min(want, need));
+  hipLaunchKernelGGL((scan_mfma_kernel<HR, KS, HG>), dim3(grid), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t *>(a.kr_pooled), reinterpret_cast<const uint16_t *>(a.qr),
+                     row_score, a.n_pool, a.batch, a.q_tokens);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan_narrow(const msa_route_args &a, float *row_score, hipStream_t s) {
+  const int ks = a.router_dim / 32;
+  switch (a.n_router_heads * 8 + ks) {
+    case 1 * 8 + 2: return launch_scan_mfma<1, 2>(a, row_score, s);
+    case 1 * 8 + 4: return launch_scan_mfma<1, 4>(a, row_score, s);
+    case 2 * 8 + 2: return launch_scan_mfma<2, 2>(a, row_score, s);
+    case 2 * 8 + 4: return launch_scan_mfma<2, 4>(a, row_score, s);
+    case 4 * 8 + 2: return launch_scan_mfma<4, 2>(a, row_score, s);
+    case 4 * 8 + 4: return launch_scan_mfma<4, 4>(a, row_score, s);
+    case 8 * 8 + 2: return launch_scan_mfma<8, 2>(a, row_score, s);
+    case 8 * 8 + 4: return launch_scan_mfma<8, 4>(a, row_score, s);
+    case 16 * 8 + 2: return launch_scan_mfma<16, 2>(a, row_score, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace msa

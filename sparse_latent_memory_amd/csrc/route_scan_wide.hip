@@ -1,0 +1,373 @@
+// Routing, stage 2 of the method: the bank scan for more than 8 bf16 query
+// tokens (prefill routing, or many decode queries batched) on MFMA, and the
+// fp32 scan on the VALU.
+//
+// Method: "EverMind-AI/MSA: Memory Sparse Attention for 100M-Token Contexts"
+// (hysenlabs.com), section "How MSA compresses and routes documents": the
+// score of a pooled row is the cosine of the routing query and the pooled
+// router key, averaged over router heads and maximised over query tokens.
+// Output of every scan: row_score[b, j] = max over query b's tokens.
+#include "msa_internal.h"
+
+#include <algorithm>
+
+namespace msa {
+namespace {
+
+constexpr int kWaves = 4;            // waves per workgroup
+
+// --------------------------------------------------------------------------
+// fp32 unit queries (VALU scan, and input of the wide fragments): qhat[m, h*dr + i] =
+//     qr[m,h,i] / max(|qr[m,h]|, eps) / Hr.
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void prep_unit_kernel(const T *__restrict__ qr, float *__restrict__ qhat, int M,
+                                                        int Hr, int dr) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int mh = blockIdx.x * kWaves + wave; mh < M * Hr; mh += gridDim.x * kWaves) {
+    const T *src = qr + (int64_t)mh * dr;
+    float ss = 0.f;
+    for (int i = lane; i < dr; i += 64) {
+      const float x = Elt<T>::get(src, i);
+      ss += x * x;
+    }
+    ss = wave_sum(ss);
+    const float scale = 1.0f / (fmaxf(sqrtf(ss), kEps) * (float)Hr);
+    for (int i = lane; i < dr; i += 64) qhat[(int64_t)mh * dr + i] = Elt<T>::get(src, i) * scale;
+  }
+}
+
+// --------------------------------------------------------------------------
+// bf16 MFMA scan for many query tokens (more than 8)
+// --------------------------------------------------------------------------
+// The query side is laid out in M-tiles of 16 rows (one bf16-rounded unit
+// query token per row).  With one token per query (Tq == 1) a tile holds 16
+// queries.  Otherwise every query gets ceil(Tq/16) tiles of its own and the
+// rows past its last token repeat that token, which leaves the max over
+// tokens unchanged.  wide_frag[mt][f][lane] is fragment f = h*KS + s of tile
+// mt in the lane layout of the narrow scan.
+__global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict__ qhat, u32x4 *__restrict__ frag,
+                                                        int B, int Tq, int Hr, int dr, int n_mt) {
+  const int KS = dr / 32, NF = Hr * KS;
+  const int mtq = (Tq + 15) / 16;
+  const int64_t n = (int64_t)n_mt * NF * 64;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(idx & 63);
+    const int f = (int)((idx >> 6) % NF);
+    const int mt = (int)((idx >> 6) / NF);
+    const int h = f / KS, s = f % KS, r = l & 15;
+    int m = -1;                               // query token of this row, or none
+    if (Tq == 1) {
+      const int b = mt * 16 + r;
+      if (b < B) m = b;
+    } else {
+      const int b = mt / mtq;
+      const int t = min((mt % mtq) * 16 + r, Tq - 1);
+      m = b * Tq + t;
+    }
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (m >= 0) {
+      const float *src = qhat + ((int64_t)m * Hr + h) * dr + 32 * s + 8 * (l >> 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e >> 1] |= (uint32_t)f32_to_bf16(src[e]) << (16 * (e & 1));
+    }
+    u32x4 o;
+    o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
+    frag[idx] = o;
+  }
+}
+
+// One workgroup of 8 waves per CU (two per SIMD).  The workgroup keeps one
+// chunk of NM query M-tiles in LDS (at most 128 KiB) for the whole launch;
+// every wave streams 16-row bank tiles from HBM one head at a time, loading
+// the next head (or the next tile's first head) into the other of two
+// fragment buffers while it computes: per head, 4 MFMAs give the tile's Gram
+// matrix (norms on its diagonal) and each of the NM query tiles takes 4
+// MFMAs against A-fragments read from LDS, scaled by the head's inverse norm.
+// Tiles of a chunk past its last real one are staged as zeros and their
+// results dropped, so the MFMA loop has no branches.
+// When the query tiles span several chunks, chunks go to different
+// workgroups of one XCD that walk the same bank tiles in the same order, so
+// the bank is fetched from HBM about once and re-read from the XCD's L2 or
+// the MALL; workgroups are dispatched round-robin over the 8 XCDs, which the
+// XCD-major logical id below follows.
+constexpr int kWideWaves = 8;
+
+template <int HR, int KS, int NM>
+__global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(const uint16_t *__restrict__ kr,
+                                                                    const u32x4 *__restrict__ frag,
+                                                                    float *__restrict__ row_score, int64_t n_pool,
+                                                                    int B, int Tq) {
+  constexpr int NF = HR * KS;
+  constexpr int ROW = NF * 32;
+  static_assert(NM <= wide_mg(NF, KS), "query chunk exceeds the LDS budget");
+  __shared__ u32x4 afrag[NM * NF * 64];
+  if (n_pool <= 0) return;              // (rejected by the API; the loads below clamp to row n_pool-1)
+  const WideLayout L = wide_layout(B, Tq, wide_mg(NF, KS));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int diag_src = ((col >> 2) << 4) + col;
+
+  const int nwg = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = nwg >> 3, rem = nwg & 7;
+  const int lid = xcd * per + min(xcd, rem) + slot;
+  int S, stream, c0, cstep;
+  if (L.n_chunks <= nwg) {
+    S = nwg / L.n_chunks;               // bank streams, each scanned once per chunk
+    stream = lid / L.n_chunks;
+    c0 = lid % L.n_chunks;
+    cstep = L.n_chunks;
+    if (stream >= S) return;            // whole workgroup: no barrier is left waiting
+  } else {
+    S = 1; stream = 0; c0 = lid; cstep = nwg;
+  }
+  const int64_t n_tiles = (n_pool + 15) >> 4;
+  const int64_t n_groups = (n_tiles + kWideWaves - 1) / kWideWaves;
+
+  // fragments of head h of this wave's tile in group g (rows past the bank
+  // end read its last row; groups past the end read the last group)
+  auto load = [&](int64_t g, int h, u32x4 *dst) {
+    g = g < n_groups ? g : n_groups - 1;
+    int64_t row = (g * kWideWaves + wave) * 16 + col;
+    row = row < n_pool ? row : n_pool - 1;
+    const uint16_t *rp = kr + row * ROW + h * KS * 32 + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) dst[s] = ld16(rp + 32 * s);
+  };
+  // One head of the tile: the query fragments are read from LDS in one batch
+  // ahead of the MFMAs (the scheduling barrier keeps the compiler from
+  // pairing each read with its MFMA), the Gram MFMAs covering their latency.
+  auto head = [&](int h, const u32x4 *f, f32x4 *acc) {
+    u32x4 a[NM][KS];
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[mt][s] = afrag[(mt * NF + h * KS + s) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, f[s]);
+      gm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, bv, gm, 0, 0, 0);
+    }
+    f32x4 d[NM];
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) d[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+        d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][s]),
+                                                        __builtin_bit_cast(bf16x8, f[s]), d[mt], 0, 0, 0);
+    const int di = col & 3;              // selects, not branches: the body stays one basic block
+    float mine = gm[0];
+    mine = di == 1 ? gm[1] : mine;
+    mine = di == 2 ? gm[2] : mine;
+    mine = di == 3 ? gm[3] : mine;
+    const float inv = rsqrtf(fmaxf(__shfl(mine, diag_src, 64), kEps2));
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) acc[mt] += d[mt] * inv;
+  };
+
+  // row scores of one bank tile: Tq == 1 stores every query's score; Tq > 1
+  // stores per query the max over the chunk's tiles of that query
+  auto epilogue = [&](int t0, int nm, int part, int64_t row, const f32x4 *acc) {
+    if (L.tok1) {
+      // rows 4*grp + i of tile t are queries 16 t + 4 grp + i
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = (t0 + mt) * 16 + 4 * grp + i;
+          if (mt < nm && b < B) row_score[(int64_t)b * n_pool + row] = acc[mt][i];
+        }
+      }
+    } else {
+      float qmax = -INFINITY;         // max over the chunk's tiles of one query
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) {
+        float m = fmaxf(fmaxf(acc[mt][0], acc[mt][1]), fmaxf(acc[mt][2], acc[mt][3]));
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        qmax = fmaxf(qmax, m);
+        const int t = t0 + mt;
+        if (mt < nm && ((t + 1) % L.mtq == 0 || mt == nm - 1)) {
+          if (grp == 0) row_score[((int64_t)(t / L.mtq) * L.n_parts + part) * n_pool + row] = qmax;
+          qmax = -INFINITY;
+        }
+      }
+    }
+  };
+
+  for (int c = c0; c < L.n_chunks; c += cstep) {
+    int t0, t1;
+    wide_chunk(L, c, &t0, &t1);
+    const int nm = t1 - t0;
+    __syncthreads();                    // readers of the previous chunk are done
+    for (int i = threadIdx.x; i < NM * NF * 64; i += blockDim.x)
+      afrag[i] = i < nm * NF * 64 ? frag[(int64_t)t0 * NF * 64 + i] : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    const int part = L.ppq > 1 ? c % L.ppq : 0;
+
+    u32x4 fa[KS], fb[KS];
+    load(stream, 0, fa);
+    for (int64_t g = stream; g < n_groups; g += S) {
+      const int64_t row = (g * kWideWaves + wave) * 16 + col;
+      f32x4 acc[NM];
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (HR == 1) {
+        load(g + S, 0, fb);
+        __builtin_amdgcn_sched_barrier(0);   // the prefetch stays ahead of the compute
+        head(0, fa, acc);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) fa[s] = fb[s];
+      } else {
+        // two heads per step, fa and fb alternating; fa ends on the next tile's head 0
+#pragma unroll 1
+        for (int h = 0; h < HR; h += 2) {
+          load(g, h + 1, fb);
+          __builtin_amdgcn_sched_barrier(0);   // the prefetch stays ahead of the compute
+          head(h, fa, acc);
+          const bool last = h + 2 >= HR;       // no branch: the loads stay where they are written
+          load(last ? g + S : g, last ? 0 : h + 2, fa);
+          __builtin_amdgcn_sched_barrier(0);
+          head(h + 1, fb, acc);
+        }
+      }
+      if (row < n_pool) epilogue(t0, nm, part, row, acc);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// VALU scan (fp32): one wave per row
+// --------------------------------------------------------------------------
+template <typename T, int EPL>
+__global__ __launch_bounds__(256) void scan_valu_kernel(const T *__restrict__ kr, const float *__restrict__ qhat,
+                                                        float *__restrict__ row_score, int64_t n_pool, int B,
+                                                        int Tq, int lanes_per_head) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rowlen = (int64_t)EPL * 64;
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave; row < n_pool; row += (int64_t)gridDim.x * kWaves) {
+    const T *rp = kr + row * rowlen + lane * EPL;
+    float x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = Elt<T>::get(rp, e);
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) n2 += x[e] * x[e];
+    for (int o = 1; o < lanes_per_head; o <<= 1) n2 += __shfl_xor(n2, o, 64);
+    const float inv = rsqrtf(fmaxf(n2, kEps2));
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] *= inv;
+    for (int b = 0; b < B; ++b) {
+      float best = -INFINITY;
+      for (int t = 0; t < Tq; ++t) {
+        const float *q = qhat + ((int64_t)(b * Tq + t)) * rowlen + lane * EPL;
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) p += q[e] * x[e];
+        best = fmaxf(best, wave_sum(p));
+      }
+      if (lane == 0) row_score[(int64_t)b * n_pool + row] = best;
+    }
+  }
+}
+
+template <int HR, int KS, int NM>
+hipError_t launch_wide_nm(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s) {
+  // one workgroup per CU (the query chunk takes most of the LDS)
+  hipLaunchKernelGGL((scan_wide_kernel<HR, KS, NM>), dim3(device_info().n_cu), dim3(kWideWaves * 64), 0, s,
+                     reinterpret_cast<const uint16_t *>(a.kr_pooled), frag, row_score, a.n_pool, a.batch,
+                     a.q_tokens);
+  return hipGetLastError();
+}
+
+// NM = the largest chunk, rounded up to a power of two (at most the LDS budget)
+template <int HR, int KS>
+hipError_t launch_wide_t(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s) {
+  constexpr int MG = wide_mg(HR * KS, KS);
+  const WideLayout L = wide_layout(a.batch, a.q_tokens, MG);
+  int need = 0;
+  for (int c = 0; c < L.n_chunks && need < MG; ++c) {
+    int t0, t1;
+    wide_chunk(L, c, &t0, &t1);
+    need = std::max(need, t1 - t0);
+  }
+  if (need <= 1) return launch_wide_nm<HR, KS, 1>(a, frag, row_score, s);
+  if (need <= 2 || MG < 4) return launch_wide_nm<HR, KS, (MG < 2 ? MG : 2)>(a, frag, row_score, s);
+  if (need <= 4 || MG < 8) return launch_wide_nm<HR, KS, (MG < 4 ? MG : 4)>(a, frag, row_score, s);
+  return launch_wide_nm<HR, KS, (MG < 8 ? MG : 8)>(a, frag, row_score, s);
+}
+
+template <typename T, int EPL>
+hipError_t launch_valu_t(const msa_route_args &a, const float *qhat, float *row_score, hipStream_t s) {
+  const int64_t need = (a.n_pool + kWaves - 1) / kWaves;
+  const int64_t want = (int64_t)device_info().n_cu * 8;
+  const int grid = (int)std::max<int64_t>(1, std::min(want, need));
+  const int lanes_per_head = 64 / a.n_router_heads;
+  hipLaunchKernelGGL((scan_valu_kernel<T, EPL>), dim3(grid), dim3(256), 0, s,
+                     reinterpret_cast<const T *>(a.kr_pooled), qhat, row_score, a.n_pool, a.batch, a.q_tokens,
+                     lanes_per_head);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_valu(const msa_route_args &a, const float *qhat, float *row_score, hipStream_t s) {
+  switch (a.n_router_heads * a.router_dim / 64) {
+    case 1: return launch_valu_t<T, 1>(a, qhat, row_score, s);
+    case 2: return launch_valu_t<T, 2>(a, qhat, row_score, s);
+    case 4: return launch_valu_t<T, 4>(a, qhat, row_score, s);
+    case 8: return launch_valu_t<T, 8>(a, qhat, row_score, s);
+    case 16: return launch_valu_t<T, 16>(a, qhat, row_score, s);
+    case 32: return launch_valu_t<T, 32>(a, qhat, row_score, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep_unit(const msa_route_args &a, float *qhat, hipStream_t s) {
+  const int M = a.batch * a.q_tokens;
+  const int n = M * a.n_router_heads;
+  const int grid = std::max(1, std::min((n + kWaves - 1) / kWaves, 1024));
+  if (a.dtype == MSA_BF16)
+    hipLaunchKernelGGL(prep_unit_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t *>(a.qr), qhat, M, a.n_router_heads, a.router_dim);
+  else
+    hipLaunchKernelGGL(prep_unit_kernel<float>, dim3(grid), dim3(256), 0, s, reinterpret_cast<const float *>(a.qr),
+                       qhat, M, a.n_router_heads, a.router_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_wide(const msa_route_args &a, const float *qhat, u32x4 *frag, hipStream_t s) {
+  const int n_mt = wide_tiles(a.batch, a.q_tokens);
+  const int64_t n = (int64_t)n_mt * a.n_router_heads * (a.router_dim / 32) * 64;
+  hipLaunchKernelGGL(prep_wide_kernel, dim3((int)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s, qhat,
+                     frag, a.batch, a.q_tokens, a.n_router_heads, a.router_dim, n_mt);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s) {
+  switch (a.n_router_heads * 8 + a.router_dim / 32) {
+    case 1 * 8 + 2: return launch_wide_t<1, 2>(a, frag, row_score, s);
+    case 1 * 8 + 4: return launch_wide_t<1, 4>(a, frag, row_score, s);
+    case 2 * 8 + 2: return launch_wide_t<2, 2>(a, frag, row_score, s);
+    case 2 * 8 + 4: return launch_wide_t<2, 4>(a, frag, row_score, s);
+    case 4 * 8 + 2: return launch_wide_t<4, 2>(a, frag, row_score, s);
+    case 4 * 8 + 4: return launch_wide_t<4, 4>(a, frag, row_score, s);
+    case 8 * 8 + 2: return launch_wide_t<8, 2>(a, frag, row_score, s);
+    case 8 * 8 + 4: return launch_wide_t<8, 4>(a, frag, row_score, s);
+    case 16 * 8 + 2: return launch_wide_t<16, 2>(a, frag, row_score, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_valu(const msa_route_args &a, const float *qhat, float *row_score, hipStream_t s) {
+  return a.dtype == MSA_BF16 ? launch_valu<uint16_t>(a, qhat, row_score, s)
+                             : launch_valu<float>(a, qhat, row_score, s);
+}
+
+}  // namespace msa

@@ -170,16 +170,30 @@ def test_route_vector_path_fp32(b, tq):
     _route_check(kr, off, qr, 8, f"valu B{b} Tq{tq}")
 
 
-@pytest.mark.parametrize("hr,dr", [(8, 128), (4, 64), (16, 64), (1, 128)])
+@pytest.mark.parametrize("hr,dr", [(8, 128), (4, 64), (16, 64), (1, 128), (8, 64), (2, 64)])
 @pytest.mark.parametrize("b,tq", [(1, 16), (4, 3), (9, 1), (20, 1), (3, 40), (100, 1), (1, 256)])
 def test_route_many_tokens_matrix_core_path(hr, dr, b, tq):
-    """More than 8 query tokens: bf16 query M-tiles through LDS (restaged
-    when they exceed one LDS load), tokens of a query padded to whole tiles."""
+    """More than 8 query tokens: bf16 query M-tiles held in LDS, tokens of a
+    query padded to whole tiles.  The shapes cover one and several chunks of
+    resident tiles (4 or 8 per chunk, by head shape), chunks of whole
+    queries, and one query cut into partial maxima over several chunks."""
     g = torch.Generator().manual_seed(hr * 1000 + dr + b * 7 + tq)
     kr, off = _ragged_bank(g, 600, 4, hr, dr, torch.bfloat16)
     qr = _randn(g, b, tq, hr, dr, dtype=torch.bfloat16).to(DEV)
     _say(f"route: wide MFMA path Hr={hr} dr={dr} B={b} Tq={tq} rows={off[-1]}")
     _route_check(kr, off, qr, 8, f"wide {hr}x{dr} B{b} Tq{tq}")
+
+
+@pytest.mark.parametrize("b,tq", [(257, 64), (65, 256)])
+def test_route_more_query_chunks_than_workgroups(b, tq):
+    """More chunks of query tiles than workgroups (one per compute unit):
+    each workgroup walks several chunks, restaging the query tiles between
+    them; with 256 tokens every query is also cut into partial maxima."""
+    g = torch.Generator().manual_seed(b + tq)
+    kr, off = _ragged_bank(g, 100, 4, 8, 128, torch.bfloat16)
+    qr = _randn(g, b, tq, 8, 128, dtype=torch.bfloat16).to(DEV)
+    _say(f"route: wide MFMA path B={b} Tq={tq} rows={off[-1]}")
+    _route_check(kr, off, qr, 8, f"wide chunks B{b} Tq{tq}")
 
 
 def test_route_prefill_config_full_size():
