@@ -172,6 +172,9 @@ def main():
                          "(this bench with FETCH_SIZE, with WRITE_SIZE; --calibrate-copy with each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--workload", default="bank-100M", choices=sorted(WORKLOADS),
+                    help="bank-100M (default, the headline line); the others print supporting lines")
+    ap.add_argument("--reps", type=int, default=10, help="timed repetitions of a supporting workload")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -187,6 +190,9 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     msa.load()
+    if args.workload != "bank-100M":
+        WORKLOADS[args.workload](args, dev)
+        return
     cfg = synth.config(4)
     K, W = args.steps, args.warmup
     n_steps = W + K + args.latency_steps
@@ -333,6 +339,247 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+# --------------------------------------------------------------------------
+# supporting workloads (one JSON line each; not the headline line)
+# --------------------------------------------------------------------------
+
+class StreamEvents:
+    """Event pairs on torch's current stream (the stream the library runs on here)."""
+
+    def __init__(self, n):
+        self.pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def ms(self, i):
+        a, b = self.pairs[i]
+        return a.elapsed_time(b)
+
+
+def _supporting_line(metric, value, unit, workload, roofline, extra, higher=True):
+    res = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "higher_is_better": higher,
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": {"workload": workload},
+           "roofline": roofline}
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+
+
+def workload_interleave(args, dev):
+    """Memory interleave at 50M tokens: 64 queries x 3 rounds.  A round routes
+    a fresh one-token query per sequence over the whole bank (the wide MFMA
+    scan), appends the top-8 documents' pooled K/V from pinned host memory to
+    each query's memory (device-side gather), and runs one decode step over
+    [memory ; 4096 local tokens] with the query offset by 8 per round so far.
+    The memory is reset at the start of every repetition."""
+    cfg = synth.config(5)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    n_docs, n_pool = len(lens), int(off[-1])
+    log(f"interleave bank: {n_docs} docs, {int(lens.sum())} tokens, {n_pool} pooled rows")
+    kr = synth.pooled_router_bank(cfg, lens, device=dev)
+    host_kv = synth.pooled_content_bank(cfg, lens, device=dev, pin=True)
+    off_d = torch.as_tensor(off, device=dev)
+    k, B = cfg.top_k, cfg.batch
+    mem_cap = cfg.ctx_cap - cfg.local_len
+    asm = msa.Assembly.allocate(host_kv, torch.as_tensor(off), B, k, mem_cap, dev)
+    lk, lv = synth.local_context(cfg, device=dev)
+    loc_len = torch.full((B,), cfg.local_len, dtype=torch.int32, device=dev)
+    R = cfg.rounds
+    qrs = [synth.router_queries(cfg, step=r, device=dev) for r in range(R)]
+    qs = [synth.decode_queries(cfg, step=r, device=dev) for r in range(R)]
+    pos = [torch.full((B,), k * (r + 1), dtype=torch.int32, device=dev) for r in range(R)]
+    rws = torch.empty(msa.route_workspace_bytes(torch.bfloat16, B, 1, cfg.n_router_heads, cfg.router_dim, n_docs,
+                                                n_pool, k), dtype=torch.uint8, device=dev)
+    dws = torch.empty(msa.decode_workspace_bytes(B, cfg.n_q_heads, cfg.head_dim, mem_cap, cfg.local_len),
+                      dtype=torch.uint8, device=dev)
+    dsc = torch.empty((B, n_docs), dtype=torch.float32, device=dev)
+    tki = torch.empty((B, k), dtype=torch.int32, device=dev)
+    tks = torch.empty((B, k), dtype=torch.float32, device=dev)
+    out = torch.empty((B, cfg.n_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, cfg.n_q_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    reps = args.reps
+    scan_ev = HipEvents(reps * R)
+    route_ev, dec_ev = StreamEvents(reps * R), StreamEvents(reps * R)
+    mem_rows = np.zeros((reps, R + 1), dtype=np.int64)
+
+    def one(rep, timed):
+        for r in range(R):
+            i = rep * R + r
+            asm.append = r > 0
+            if timed:
+                route_ev.pairs[i][0].record(stream)
+            msa.route(qrs[r], kr, off_d, k, dsc, tki, tks, rws, assembly=asm, stream=stream,
+                      prof_events=scan_ev.pairs[i] if timed else None)
+            if timed:
+                route_ev.pairs[i][1].record(stream)
+                dec_ev.pairs[i][0].record(stream)
+            msa.sparse_decode(qs[r], asm.mem_kv, asm.mem_len, lk, lv, loc_len, pos[r], cfg.rope_theta, out, lse,
+                              dws, stream=stream)
+            if timed:
+                dec_ev.pairs[i][1].record(stream)
+                mem_rows[rep, r + 1] = int(asm.mem_len.sum())   # synchronises: outside the timed events
+
+    for _ in range(2):
+        one(0, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for rep in range(reps):
+        one(rep, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan = np.array([[scan_ev.elapsed_ms(rep * R + r) for r in range(R)] for rep in range(reps)])
+    route = np.array([[route_ev.ms(rep * R + r) for r in range(R)] for rep in range(reps)])
+    dec = np.array([[dec_ev.ms(rep * R + r) for r in range(R)] for rep in range(reps)])
+    kv_row = 2 * cfg.n_kv_heads * cfg.head_dim * 2
+    scan_bytes = n_pool * cfg.n_router_heads * cfg.router_dim * 2
+    rows_after = mem_rows[:, 1:].mean(0)
+    dec_bytes = (rows_after + B * cfg.local_len) * kv_row
+    gathered = np.diff(mem_rows, axis=1).mean(0) * kv_row
+    per_round = []
+    for r in range(R):
+        per_round.append({
+            "round": r + 1, "scan_us": float(scan[:, r].mean() * 1e3),
+            "scan_GBs": float(scan_bytes / (scan[:, r].mean() / 1e3) / 1e9),
+            "route_us": float(route[:, r].mean() * 1e3),
+            "select_gather_us": float((route[:, r] - scan[:, r]).mean() * 1e3),
+            "gathered_bytes": float(gathered[r]), "memory_rows": float(rows_after[r]),
+            "decode_us": float(dec[:, r].mean() * 1e3),
+            "decode_GBs": float(dec_bytes[r] / (dec[:, r].mean() / 1e3) / 1e9)})
+    round_ms = (route + dec).mean()
+    achieved = scan_bytes / (scan.mean() / 1e3) / 1e9
+    _supporting_line(
+        "query-rounds/s (route + gather + decode), memory interleave", B * R * reps / wall, "query-rounds/s",
+        f"interleave-50M: {n_docs} docs, {int(lens.sum())} tokens (lognormal, mean 1024), {n_pool} pooled rows; "
+        f"64 queries x {R} rounds of top-{k}, memory <= {mem_cap} rows + {cfg.local_len} local tokens, "
+        "GQA 32/8 x 128",
+        {"kernel": "route bank scan, 64 one-token queries (scan_wide_kernel<8, 4, 4>)", "bound": "hbm",
+         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+         "traffic": None},
+        {"ms_per_round": float(round_ms), "rounds": per_round, "reps": reps})
+
+
+def workload_prefill(args, dev):
+    """The 2048-document routing-layer workload: encode the raw 1.31M-token
+    bank (document-wise RoPE + chunk means), route one 256-token query
+    prefill over it (wide MFMA scan), gather the top-16 and decode one step
+    over [memory ; 2048 local tokens].  The bank is 44.6 MB, so the scan runs
+    out of the MALL: reported as warm."""
+    cfg = synth.config(2)
+    bank = synth.raw_bank(cfg, device=dev)
+    lens = bank["lens"]
+    off = synth.row_offsets(lens, cfg.pool)
+    n_docs, n_pool, n_tok = len(lens), int(off[-1]), int(lens.sum())
+    log(f"prefill bank: {n_docs} docs, {n_tok} tokens, {n_pool} pooled rows")
+    off_d = torch.as_tensor(off, device=dev)
+    kv = torch.empty((n_pool, 2, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    krp = torch.empty((n_pool, cfg.n_router_heads, cfg.router_dim), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    reps = args.reps
+    pool_ev = StreamEvents(reps)
+    for _ in range(2):
+        msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], off_d, cfg.pool, cfg.rope_theta,
+                        n_pool, kv, krp, stream=stream)
+    for i in range(reps):
+        pool_ev.pairs[i][0].record(stream)
+        msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], off_d, cfg.pool, cfg.rope_theta,
+                        n_pool, kv, krp, stream=stream)
+        pool_ev.pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    pool_ms = np.mean([pool_ev.ms(i) for i in range(reps)])
+    elt = 2
+    pool_read = n_tok * (2 * cfg.n_kv_heads * cfg.head_dim + cfg.n_router_heads * cfg.router_dim) * elt
+    pool_write = n_pool * (2 * cfg.n_kv_heads * cfg.head_dim + cfg.n_router_heads * cfg.router_dim) * elt
+    pool_gbs = (pool_read + pool_write) / (pool_ms / 1e3) / 1e9
+
+    host_kv = kv.cpu().pin_memory()
+    k = cfg.top_k
+    mem_cap = 512
+    asm = msa.Assembly.allocate(host_kv, torch.as_tensor(off), 1, k, mem_cap, dev)
+    qr = synth.router_queries(cfg, device=dev)
+    q = synth.decode_queries(cfg, device=dev)
+    lk, lv = synth.local_context(cfg, device=dev)
+    loc_len = torch.full((1,), cfg.local_len, dtype=torch.int32, device=dev)
+    pos = torch.full((1,), k, dtype=torch.int32, device=dev)
+    rws = torch.empty(msa.route_workspace_bytes(torch.bfloat16, 1, cfg.q_tokens, cfg.n_router_heads, cfg.router_dim,
+                                                n_docs, n_pool, k), dtype=torch.uint8, device=dev)
+    scan_ev = HipEvents(reps)
+    route_ev, dec_ev = StreamEvents(reps), StreamEvents(reps)
+    for i in range(-2, reps):
+        if i >= 0:
+            route_ev.pairs[i][0].record(stream)
+        msa.route(qr, krp, off_d, k, workspace=rws, assembly=asm, stream=stream,
+                  prof_events=scan_ev.pairs[i] if i >= 0 else None)
+        if i >= 0:
+            route_ev.pairs[i][1].record(stream)
+            dec_ev.pairs[i][0].record(stream)
+        msa.sparse_decode(q, asm.mem_kv, asm.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, stream=stream)
+        if i >= 0:
+            dec_ev.pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    scan_ms = np.mean([scan_ev.elapsed_ms(i) for i in range(reps)])
+    flops = 2.0 * cfg.q_tokens * n_pool * cfg.n_router_heads * cfg.router_dim
+    tfs = flops / (scan_ms / 1e3) / 1e12
+    _supporting_line(
+        "pooled tokens/s (encode) and prefill routing", n_tok / (pool_ms / 1e3), "tokens/s",
+        f"prefill-1M: {n_docs} docs, lengths U[256,1024], {n_tok} raw tokens -> {n_pool} pooled rows, "
+        "K/V 8x128 + Kr 8x128 bf16; 256-token routing query, top-16, decode GQA 32/8x128 over 2048 local tokens",
+        {"kernel": "pool_kernel<bf16> (encode)", "bound": "hbm", "achieved": pool_gbs, "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": pool_gbs / HBM_PEAK_GBS, "traffic": None},
+        {"encode_us": float(pool_ms * 1e3), "encode_bytes": pool_read + pool_write,
+         "routing": {"kernel": "scan_wide_kernel<8, 4, 4>", "bound": "mfma", "scan_us": float(scan_ms * 1e3),
+                     "achieved_TFs": tfs, "peak_TFs": 2500.0, "frac": tfs / 2500.0, "bank": "MALL-warm (44.6 MB)",
+                     "route_us": float(np.mean([route_ev.ms(i) for i in range(reps)]) * 1e3)},
+         "decode_us": float(np.mean([dec_ev.ms(i) for i in range(reps)]) * 1e3), "reps": reps})
+
+
+def workload_needles(args, dev):
+    """The 16.7M-token bank with 8 one-token queries, each with a planted
+    needle (one pooled row at per-head cosine 0.6): scan + top-16, and the
+    fraction of queries whose needle document is selected."""
+    cfg = synth.config(3)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    n_docs, n_pool = len(lens), int(off[-1])
+    log(f"needle bank: {n_docs} docs, {int(lens.sum())} tokens, {n_pool} pooled rows")
+    kr = synth.pooled_router_bank(cfg, lens, device=dev)
+    qr = synth.router_queries(cfg, device=dev)
+    needles = synth.plant_needles(cfg, qr, kr, off)
+    off_d = torch.as_tensor(off, device=dev)
+    k = cfg.top_k
+    rws = torch.empty(msa.route_workspace_bytes(torch.bfloat16, cfg.batch, 1, cfg.n_router_heads, cfg.router_dim,
+                                                n_docs, n_pool, k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    reps = args.reps
+    scan_ev = HipEvents(reps)
+    route_ev = StreamEvents(reps)
+    for i in range(-2, reps):
+        if i >= 0:
+            route_ev.pairs[i][0].record(stream)
+        idx, _, _ = msa.route(qr, kr, off_d, k, workspace=rws, stream=stream,
+                              prof_events=scan_ev.pairs[i] if i >= 0 else None)
+        if i >= 0:
+            route_ev.pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    found = float(np.mean([needles[b] in set(idx[b].cpu().tolist()) for b in range(cfg.batch)]))
+    scan_ms = np.mean([scan_ev.elapsed_ms(i) for i in range(reps)])
+    route_ms = np.mean([route_ev.ms(i) for i in range(reps)])
+    scan_bytes = n_pool * cfg.n_router_heads * cfg.router_dim * 2
+    achieved = scan_bytes / (scan_ms / 1e3) / 1e9
+    _supporting_line(
+        "bank tokens scored/s, 8 queries with planted needles", cfg.batch * int(lens.sum()) / (route_ms / 1e3),
+        "bank tokens/s",
+        f"needles-16M: {n_docs} docs, {int(lens.sum())} tokens (lognormal, mean 512), {n_pool} pooled rows, "
+        "8 one-token queries, top-16",
+        {"kernel": "route bank scan, 8 one-token queries (scan_mfma_kernel<8, 4, 1>)", "bound": "hbm",
+         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+         "traffic": None},
+        {"scan_us": float(scan_ms * 1e3), "route_us": float(route_ms * 1e3), "needle_recall_top16": found,
+         "reps": reps})
+
+
+WORKLOADS = {"bank-100M": None, "interleave-50M": workload_interleave, "prefill-1M": workload_prefill,
+             "needles-16M": workload_needles}
 
 
 def cpu_baseline(cfg, kr, pool_off, qr, seconds):

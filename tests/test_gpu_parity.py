@@ -512,6 +512,56 @@ def test_end_to_end_bf16_ragged():
     _chain(cfg, lens, 6, 64, 64, 6)
 
 
+@pytest.mark.parametrize("mem_cap", [12288, 200])
+def test_interleave_rounds_end_to_end(mem_cap):
+    """Memory interleave: 3 rounds of route -> append -> decode for 64
+    queries over a ragged lognormal bank.  Round r routes a fresh query,
+    appends its top-8 documents to the query's memory (documents that no
+    longer fit are dropped with every lower-ranked one) and decodes with the
+    query offset by 8 per round so far.  Every round is checked against the
+    oracle: scores, top-k, the assembled memory byte for byte, and the decode
+    output on that memory.  mem_cap 200 forces drops in later rounds."""
+    cfg = synth.config(5, total_tokens=1_500_000, local_len=256)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    _say(f"interleave: 64 queries x 3 rounds, {len(lens)} docs, {off[-1]} rows, mem_cap {mem_cap}")
+    kr = synth.pooled_router_bank(cfg, lens, device=DEV)
+    host_kv = synth.pooled_content_bank(cfg, lens, device=DEV, pin=True)
+    k = cfg.top_k
+    asm = msa.Assembly.allocate(host_kv, torch.as_tensor(off), cfg.batch, k, mem_cap, DEV)
+    lk, lv = synth.local_context(cfg)
+    loc_len = np.full(cfg.batch, cfg.local_len, dtype=np.int32)
+    kr_n = np64(kr)
+    src = host_kv.view(torch.int16).numpy()
+    ref_mem = np.zeros((cfg.batch, mem_cap) + src.shape[1:], dtype=np.int16)
+    ref_len = np.zeros(cfg.batch, dtype=np.int64)
+    dropped = 0
+    for rnd in range(cfg.rounds):
+        qr = synth.router_queries(cfg, step=rnd, device=DEV)
+        q = synth.decode_queries(cfg, step=rnd, device=DEV)
+        asm.append = rnd > 0
+        pos = np.full(cfg.batch, k * (rnd + 1), dtype=np.int32)
+        idx, _, dsc = msa.route(qr, kr, _dev(off), k, assembly=asm)
+        out, _ = msa.sparse_decode(q, asm.mem_kv, asm.mem_len, _dev(lk), _dev(lv), _dev(loc_len), _dev(pos),
+                                   cfg.rope_theta)
+        torch.cuda.synchronize()
+        ref = oracle.doc_scores(np64(qr), kr_n, off)
+        check_scores(np64(dsc), ref, f"round {rnd} scores")
+        check_topk(np64(idx), ref, k, f"round {rnd} top-k")
+        ref_mem, ref_len, taken = oracle.assemble(src, off, np64(idx), mem_cap, start_len=ref_len, mem=ref_mem)
+        dropped += int((taken < k).sum())
+        assert np.array_equal(np64(asm.mem_len), ref_len), f"round {rnd} memory lengths"
+        got = asm.mem_kv.view(torch.int16).cpu().numpy()
+        for b in range(cfg.batch):
+            assert np.array_equal(got[b, :ref_len[b]], ref_mem[b, :ref_len[b]]), f"round {rnd} memory of query {b}"
+        mem_f = np64(asm.mem_kv)
+        ro, _ = oracle.decode(np64(q), mem_f, ref_len, np64(lk), np64(lv), loc_len, pos, cfg.rope_theta, None,
+                              "bf16")
+        check_decode(np64(out), ro, torch.bfloat16, f"round {rnd} decode")
+    if mem_cap < 1000:
+        assert dropped > 0, "the small memory should force drops"
+
+
 def test_dense_special_case_equals_sdpa():
     """Pool size 1 and k = all documents: the whole path is dense attention
     over [every document's rotated keys ; the locally rotated keys], checked
