@@ -37,4 +37,5 @@ from .msa_oracle import (  # noqa: F401
     topk,
     assemble,
     decode,
+    attend,
 )

@@ -90,3 +90,32 @@ def decode(q, mem_k, mem_v, loc_k, loc_v, pos_offset, theta):
         outs.append([sum(w[i] * vals[i][e] for i in range(len(w))) / s for e in range(d)])
         lses.append(m + math.log(s))
     return outs, lses
+
+
+def attend(q, mem_k, mem_v, loc_k, loc_v, pos_offset, theta):
+    """A block of query tokens, one at a time.  q: [Tq][Hq][D] are the last
+    Tq of the T local tokens; token t is local token i = T - Tq + t and reads
+    the memory and the local tokens 0 .. i.  Returns (out [Tq][Hq][D],
+    lse [Tq][Hq])."""
+    n_t, t_loc = len(q), len(loc_k)
+    outs, lses = [], []
+    for t in range(n_t):
+        i = t_loc - n_t + t
+        n_q, d = len(q[t]), len(q[t][0])
+        n_kv = len(loc_k[0]) if len(loc_k) else len(mem_k[0])
+        o_t, l_t = [], []
+        for h in range(n_q):
+            g = h // (n_q // n_kv)
+            qh = _rot(list(q[t][h]), pos_offset + i, theta)
+            keys = [list(map(float, mk[g])) for mk in mem_k]
+            keys += [_rot(list(loc_k[j][g]), pos_offset + j, theta) for j in range(i + 1)]
+            vals = [list(map(float, mv[g])) for mv in mem_v] + [list(map(float, loc_v[j][g])) for j in range(i + 1)]
+            logits = [sum(a * b for a, b in zip(qh, kk)) / math.sqrt(d) for kk in keys]
+            m = max(logits)
+            w = [math.exp(x - m) for x in logits]
+            s = sum(w)
+            o_t.append([sum(w[j] * vals[j][e] for j in range(len(w))) / s for e in range(d)])
+            l_t.append(m + math.log(s))
+        outs.append(o_t)
+        lses.append(l_t)
+    return outs, lses

@@ -39,6 +39,12 @@ Readings where the pages are silent (each is also listed in the design doc):
   rotated); one softmax over [memory ; local] with scale 1/sqrt(D); query
   head h reads KV head h // (Hq / Hkv).
 * R9 every cast to bfloat16 rounds to nearest, ties to even.
+* R13 a block of Tq query tokens (prefill through the sparse context) is
+  the last Tq tokens of the local context: with T local tokens, token t of
+  the block is local token i_t = T - Tq + t at position o + i_t; it sees
+  every memory row and the local tokens 0 .. i_t (causal); Tq = 1 is the
+  decode step of R8.  The pages order the context background -> query ->
+  generation and give no block form, so this is the plainest extension.
 """
 
 import numpy as np
@@ -285,3 +291,53 @@ def decode(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset,
             out[b, h] = (w @ vals[:, g, :]) / den
             lse[b, h] = m + np.log(den)
     return round_to_storage(out, out_dtype), lse
+
+
+# --------------------------------------------------------------------------
+# a block of query tokens through the sparse context (reading R13)
+# --------------------------------------------------------------------------
+
+def attend(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset,
+           theta, scale=None, out_dtype="f64"):
+    """Attention of Tq query tokens over [pooled memory ; causal local].
+
+    q: [B, Tq, Hq, D] (before RoPE), the last Tq tokens of each local
+    context; mem_kv: [B, M_cap, 2, Hkv, D]; local_k, local_v:
+    [B, T_cap, Hkv, D] (K before RoPE); mem_len, local_len, pos_offset: [B].
+    Written as the masked definition: logits of every query row against
+    every key, keys a token may not see set to -inf, one softmax per row.
+    Returns (out [B, Tq, Hq, D] rounded to out_dtype, lse [B, Tq, Hq]
+    float64); a row that sees no key gets out = 0 and lse = -inf.
+    """
+    q = np.asarray(q, dtype=F64)
+    n_b, n_t, n_q, d = q.shape
+    n_kv = np.asarray(local_k).shape[2]
+    group = n_q // n_kv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n_b, n_t, n_q, d), dtype=F64)
+    lse = np.full((n_b, n_t, n_q), -np.inf, dtype=F64)
+    for b in range(n_b):
+        o, t_loc, m_len = int(pos_offset[b]), int(local_len[b]), int(mem_len[b])
+        i_t = t_loc - n_t + np.arange(n_t)                                  # local index of each token
+        q_rot = rope(q[b], o + i_t, theta)                                  # [Tq, Hq, D]
+        k_loc = rope(np.asarray(local_k[b, :t_loc], dtype=F64), o + np.arange(t_loc), theta)
+        keys = np.concatenate([np.asarray(mem_kv[b, :m_len, 0], dtype=F64), k_loc], axis=0)
+        vals = np.concatenate([np.asarray(mem_kv[b, :m_len, 1], dtype=F64),
+                               np.asarray(local_v[b, :t_loc], dtype=F64)], axis=0)
+        j = np.arange(m_len + t_loc)
+        visible = (j[None, :] < m_len) | ((j[None, :] - m_len) <= i_t[:, None])   # [Tq, M + T]
+        for h in range(n_q):
+            g = h // group
+            logits = scale * (q_rot[:, h, :] @ keys[:, g, :].T)             # [Tq, M + T]
+            logits = np.where(visible, logits, -np.inf)
+            for t in range(n_t):
+                if not visible[t].any():
+                    continue
+                m = logits[t].max()
+                w = np.exp(logits[t] - m)
+                den = w.sum()
+                out[b, t, h] = (w @ vals[:, g, :]) / den
+                lse[b, t, h] = m + np.log(den)
+    return round_to_storage(out, out_dtype), lse
+

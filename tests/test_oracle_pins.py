@@ -419,3 +419,99 @@ def test_decode_special_cases():
     # no keys at all
     nil, ln = oracle.decode(q, empty, [0], lk, lv, [0], [0], 1e6)
     assert np.all(nil == 0) and np.all(np.isneginf(ln))
+
+
+# --------------------------------------------------------------------------
+# a block of query tokens through the sparse context (reading R13)
+# --------------------------------------------------------------------------
+
+def test_attend_worked_example(golden_dir):
+    g = _load(golden_dir, "attend_worked_example.json")
+    out, lse = oracle.attend(np.array(g["q"]), np.array(g["mem_kv"]), g["mem_len"], np.array(g["local_k"]),
+                             np.array(g["local_v"]), g["local_len"], g["pos_offset"], g["theta"])
+    np.testing.assert_allclose(out, g["out"], atol=1e-14)
+    np.testing.assert_allclose(lse, g["lse"], atol=1e-14)
+
+
+def test_attend_one_token_is_the_decode_step():
+    hq, hkv, d = 8, 2, 16
+    q = RNG.standard_normal((2, hq, d))
+    mem = RNG.standard_normal((2, 5, 2, hkv, d))
+    lk = RNG.standard_normal((2, 7, hkv, d))
+    lv = RNG.standard_normal((2, 7, hkv, d))
+    a, la = oracle.attend(q[:, None], mem, [3, 5], lk, lv, [7, 2], [16, 1000], 1e6)
+    b, lb = oracle.decode(q, mem, [3, 5], lk, lv, [7, 2], [16, 1000], 1e6)
+    np.testing.assert_allclose(a[:, 0], b, atol=1e-12)
+    np.testing.assert_allclose(la[:, 0], lb, atol=1e-12)
+
+
+def test_attend_matches_brute_force_twin():
+    hq, hkv, d, tq = 4, 2, 8, 3
+    q = RNG.standard_normal((1, tq, hq, d))
+    mem = RNG.standard_normal((1, 4, 2, hkv, d))
+    lk = RNG.standard_normal((1, 6, hkv, d))
+    lv = RNG.standard_normal((1, 6, hkv, d))
+    out, lse = oracle.attend(q, mem, [2], lk, lv, [5], [9], 1e4)
+    o2, l2 = loops.attend(q[0], mem[0, :2, 0], mem[0, :2, 1], lk[0, :5], lv[0, :5], 9, 1e4)
+    np.testing.assert_allclose(out[0], o2, atol=1e-12)
+    np.testing.assert_allclose(lse[0], l2, atol=1e-12)
+
+
+def test_attend_dense_causal_equals_sdpa():
+    """Pool size 1, k = all documents: a block of query tokens over the
+    assembled context is torch's scaled_dot_product_attention (float64, GQA
+    by repeating KV heads) with a mask that shows every memory key and the
+    local keys up to each token."""
+    hq, hkv, d, theta = 8, 2, 16, 1e6
+    lens = np.array([3, 5, 2])
+    off = np.concatenate([[0], np.cumsum(lens)])
+    k = RNG.standard_normal((off[-1], hkv, d))
+    v = RNG.standard_normal((off[-1], hkv, d))
+    kr = RNG.standard_normal((off[-1], 2, 4))
+    kv, krp, poff = oracle.pool(k, v, kr, off, 1, theta)
+    idx, _ = oracle.topk(oracle.doc_scores(RNG.standard_normal((1, 1, 2, 4)), krp, poff), len(lens))
+    mem, mlen, _ = oracle.assemble(kv, poff, idx, mem_cap=int(off[-1]))
+    t_loc, tq = 9, 4
+    q = RNG.standard_normal((1, tq, hq, d))
+    lk = RNG.standard_normal((1, t_loc, hkv, d))
+    lv = RNG.standard_normal((1, t_loc, hkv, d))
+    o = len(lens)
+    out, _ = oracle.attend(q, mem, mlen, lk, lv, [t_loc], [o], theta)
+
+    order = idx[0]
+    keys = [oracle.rope(k[off[i]:off[i + 1]], np.arange(lens[i]), theta) for i in order]
+    keys.append(oracle.rope(lk[0], o + np.arange(t_loc), theta))
+    vals = [v[off[i]:off[i + 1]] for i in order] + [lv[0]]
+    kk = torch.from_numpy(np.concatenate(keys)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0).contiguous()
+    vv = torch.from_numpy(np.concatenate(vals)).permute(1, 0, 2).repeat_interleave(hq // hkv, 0).contiguous()
+    i_t = t_loc - tq + np.arange(tq)
+    qq = torch.from_numpy(oracle.rope(q[0], o + i_t, theta)).permute(1, 0, 2).contiguous()   # [Hq, Tq, D]
+    m = int(off[-1])
+    j = np.arange(m + t_loc)
+    mask = torch.from_numpy((j[None, :] < m) | ((j[None, :] - m) <= i_t[:, None]))
+    want = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask)   # [Hq, Tq, D]
+    np.testing.assert_allclose(out[0], want.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_attend_is_causal_and_relative():
+    hq, hkv, d, tq, t_loc = 4, 2, 8, 3, 6
+    q = RNG.standard_normal((1, tq, hq, d))
+    mem = RNG.standard_normal((1, 3, 2, hkv, d))
+    lk = RNG.standard_normal((1, t_loc, hkv, d))
+    lv = RNG.standard_normal((1, t_loc, hkv, d))
+    base, _ = oracle.attend(q, mem, [3], lk, lv, [t_loc], [5], 1e6)
+    # changing the last local token moves only the last query token
+    lk2, lv2 = lk.copy(), lv.copy()
+    lk2[0, -1] += 1.0
+    lv2[0, -1] -= 2.0
+    moved, _ = oracle.attend(q, mem, [3], lk2, lv2, [t_loc], [5], 1e6)
+    np.testing.assert_allclose(moved[0, :tq - 1], base[0, :tq - 1], atol=1e-14)
+    assert np.abs(moved[0, tq - 1] - base[0, tq - 1]).max() > 1e-3
+    # without memory the position offset cancels
+    empty = np.zeros((1, 0, 2, hkv, d))
+    a, _ = oracle.attend(q, empty, [0], lk, lv, [t_loc], [0], 1e6)
+    b, _ = oracle.attend(q, empty, [0], lk, lv, [t_loc], [777], 1e6)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+    # the first local token as the only visible key gives its value
+    one, _ = oracle.attend(q[:, :1], empty, [0], lk, lv, [1], [3], 1e6)
+    np.testing.assert_allclose(one[0, 0], np.repeat(lv[0, 0], hq // hkv, axis=0), atol=1e-14)
