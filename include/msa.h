@@ -18,6 +18,9 @@
  *   msa_sparse_decode - sparse generation: one attention step over the
  *                       assembled memory followed by the query's local K/V,
  *                       with the query position offset by k.
+ *   msa_sparse_attend - the same for a block of query tokens (prefill
+ *                       through the sparse context), causal over the local
+ *                       tokens.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -208,7 +211,10 @@ size_t msa_route_workspace_bytes(int32_t dtype, int32_t batch, int32_t q_tokens,
  * global RoPE (order: background, then query, then generation), same
  * sources as above.  A query with no keys gets out = 0, lse = -inf.
  * M and T are clamped to [0, mem_cap] and [0, local_cap].  fp32 softmax and
- * accumulation; out is rounded to nearest-even into `dtype`.
+ * accumulation; out is rounded to nearest-even into `dtype`.  bf16 runs
+ * msa_sparse_attend's matrix-core kernel with one query token (same
+ * arithmetic as described there) when q and out are 16-byte aligned; fp32,
+ * or unaligned q/out, runs a split-KV kernel in fp32 vector arithmetic.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t dtype;            /* msa_dtype of q, mem_kv, local_k/v, out       */
@@ -244,6 +250,66 @@ int msa_sparse_decode(const msa_decode_args *args, void *stream);
 /* Workspace for msa_sparse_decode, in bytes (0 on invalid sizes). */
 size_t msa_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                   int32_t mem_cap, int32_t local_cap);
+
+/* ------------------------------------------------------------------------
+ * Stage 3 for a block of query tokens - prefill through the sparse context.
+ *
+ * The Tq query tokens of query b are the LAST Tq tokens of its local context
+ * (their K/V are already in local_k/local_v).  With o = pos_offset[b],
+ * T = local_len[b], M = mem_len[b], token t sits at local index
+ * i_t = T - Tq + t and position o + i_t:
+ *   q'[t,h]  = RoPE(q[b,t,h], o + i_t)
+ *   keys     = [ mem_kv[b, 0..M, 0] (as stored) ; RoPE(local_k[b,i], o + i) ]
+ *   token t sees every memory row and the local tokens i <= i_t (causal)
+ *   out[b,t,h] = softmax(scale * keys[:, g] . q'[t,h]) . vals[:, g] over
+ *                the keys it sees; lse[b,t,h] their log-sum-exp.
+ * With Tq = 1 this is msa_sparse_decode's step.  Sources as for stage 3; the
+ * pages order the context background, then query, then generation, and do
+ * not spell out the block form: the causal block over the local context is
+ * this library's reading.  A token that sees no key gets out = 0,
+ * lse = -inf (also when T < Tq leaves it without local tokens).
+ * bf16 only: q, K and V enter v_mfma_f32_16x16x32_bf16 /
+ * v_mfma_f32_16x16x16bf16_1k with fp32 accumulation; the rotated query is
+ * split into two bf16 terms, rotated local keys and the softmax weights are
+ * rounded to bf16 once; softmax statistics are fp32.
+ * Validation as for msa_sparse_decode, plus batch, q_tokens >= 1,
+ * Hq / Hkv <= 16; fp32 returns MSA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t dtype;            /* MSA_BF16                                     */
+  int32_t batch;
+  int32_t q_tokens;         /* Tq >= 1                                      */
+  int32_t n_q_heads;        /* Hq, multiple of Hkv, Hq/Hkv <= 16            */
+  int32_t n_kv_heads;       /* Hkv                                          */
+  int32_t head_dim;         /* D in {64, 128}                               */
+  int32_t mem_cap;          /* >= 0                                         */
+  int32_t local_cap;        /* >= 0                                         */
+  const void *q;            /* device [B, Tq, Hq, D], before RoPE           */
+  const void *mem_kv;       /* device [B, mem_cap, 2, Hkv, D]; NULL if cap 0 */
+  const int32_t *mem_len;   /* device [B]                                   */
+  const void *local_k;      /* device [B, local_cap, Hkv, D], before RoPE   */
+  const void *local_v;      /* device [B, local_cap, Hkv, D]                */
+  const int32_t *local_len; /* device [B], including the Tq query tokens    */
+  const int32_t *pos_offset;/* device [B]                                   */
+  double rope_theta;        /* > 0                                          */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(D)                       */
+  int32_t reserved0;
+  void *out;                /* device out [B, Tq, Hq, D], 16-byte aligned   */
+  float *lse;               /* device out [B, Tq, Hq]; may be NULL          */
+  void *workspace;          /* device, msa_attend_workspace_bytes() bytes   */
+  size_t workspace_bytes;
+  /* profiling, optional: hipEvent_t values recorded on `stream` right before
+   * and right after the attention kernel (the split merge follows); NULL to
+   * skip */
+  void *prof_event_begin;
+  void *prof_event_end;
+} msa_attend_args;
+
+int msa_sparse_attend(const msa_attend_args *args, void *stream);
+
+/* Workspace for msa_sparse_attend, in bytes (0 on invalid sizes). */
+size_t msa_attend_workspace_bytes(int32_t batch, int32_t q_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t mem_cap, int32_t local_cap);
 
 /* Thread-local description of the last non-OK return on this thread. */
 const char *msa_last_error(void);

@@ -10,13 +10,15 @@ from . import synth  # noqa: F401
 from ._lib import (  # noqa: F401
     Assembly,
     MSAError,
+    attend_workspace_bytes,
     decode_workspace_bytes,
     load,
     pool_encode,
     route,
     route_workspace_bytes,
+    sparse_attend,
     sparse_decode,
 )
 
-__all__ = ["Assembly", "MSAError", "decode_workspace_bytes", "load", "pool_encode", "route",
-           "route_workspace_bytes", "sparse_decode", "synth"]
+__all__ = ["Assembly", "MSAError", "attend_workspace_bytes", "decode_workspace_bytes", "load", "pool_encode",
+           "route", "route_workspace_bytes", "sparse_attend", "sparse_decode", "synth"]

@@ -65,8 +65,20 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class AttendArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", I32), ("batch", I32), ("q_tokens", I32), ("n_q_heads", I32), ("n_kv_heads", I32),
+        ("head_dim", I32), ("mem_cap", I32), ("local_cap", I32),
+        ("q", P), ("mem_kv", P), ("mem_len", P), ("local_k", P), ("local_v", P), ("local_len", P),
+        ("pos_offset", P), ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
+        ("reserved0", I32), ("out", P), ("lse", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
+        ("prof_event_begin", P), ("prof_event_end", P),
+    ]
+
+
 EXPORTS = ("msa_pool_encode", "msa_route", "msa_route_workspace_bytes", "msa_sparse_decode",
-           "msa_decode_workspace_bytes", "msa_last_error", "msa_version")
+           "msa_decode_workspace_bytes", "msa_sparse_attend", "msa_attend_workspace_bytes", "msa_last_error",
+           "msa_version")
 
 _lib = None
 
@@ -91,6 +103,10 @@ def load(path=None):
     lib.msa_route_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.msa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.msa_sparse_attend.argtypes = [ctypes.POINTER(AttendArgs), P]
+    lib.msa_sparse_attend.restype = ctypes.c_int
+    lib.msa_attend_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    lib.msa_attend_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_last_error.argtypes = []
     lib.msa_last_error.restype = ctypes.c_char_p
     lib.msa_version.argtypes = []
@@ -263,3 +279,38 @@ def sparse_decode(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, r
         a.prof_event_begin, a.prof_event_end = prof_events
     _check(load().msa_sparse_decode(ctypes.byref(a), _stream(stream)))
     return out, lse
+
+
+def attend_workspace_bytes(batch, q_tokens, n_q_heads, n_kv_heads, head_dim, mem_cap, local_cap):
+    return int(load().msa_attend_workspace_bytes(batch, q_tokens, n_q_heads, n_kv_heads, head_dim, mem_cap,
+                                                 local_cap))
+
+
+def sparse_attend(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, rope_theta,
+                  out=None, lse=None, workspace=None, softmax_scale=0.0, want_lse=True, stream=None,
+                  prof_events=None):
+    """msa_sparse_attend.  q: [B, Tq, Hq, D], the last Tq local tokens of
+    each query; mem_kv: [B, M_cap, 2, Hkv, D] (or None); local_k/v:
+    [B, T_cap, Hkv, D]; mem_len, local_len, pos_offset: int32 device [B].
+    Returns (out [B, Tq, Hq, D], lse [B, Tq, Hq])."""
+    b, tq, hq, d = q.shape
+    _, t_cap, hkv, _ = local_k.shape
+    m_cap = 0 if mem_kv is None else mem_kv.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((b, tq, hq, d), dtype=q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((b, tq, hq), dtype=torch.float32, device=dev)
+    if workspace is None:
+        nbytes = attend_workspace_bytes(b, tq, hq, hkv, d, m_cap, t_cap)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    a = AttendArgs(dtype=dtype_code(q.dtype), batch=b, q_tokens=tq, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                   mem_cap=m_cap, local_cap=t_cap, q=_ptr(q), mem_kv=_ptr(mem_kv), mem_len=_ptr(mem_len),
+                   local_k=_ptr(local_k), local_v=_ptr(local_v), local_len=_ptr(local_len),
+                   pos_offset=_ptr(pos_offset), rope_theta=float(rope_theta), softmax_scale=float(softmax_scale),
+                   out=_ptr(out), lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=workspace.numel())
+    if prof_events is not None:
+        a.prof_event_begin, a.prof_event_end = prof_events
+    _check(load().msa_sparse_attend(ctypes.byref(a), _stream(stream)))
+    return out, lse
+

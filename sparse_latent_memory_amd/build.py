@@ -15,7 +15,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["msa_api.hip", "pool.hip", "route.hip", "route_scan.hip", "route_scan_wide.hip", "route_select.hip",
-           "decode.hip"]
+           "decode.hip", "attend.hip"]
 LIB = os.path.join(HERE, "libmsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 

@@ -1,0 +1,518 @@
+// Stage 3 for a block of query tokens: attention of Tq query tokens (the last
+// Tq tokens of each local context) over [pooled memory ; causal local K/V],
+// with global RoPE.  Tq = 1 is the decode step.
+//
+// Method: "EverMind-AI/MSA: Memory Sparse Attention for 100M-Token Contexts"
+// (hysenlabs.com), section "How MSA compresses and routes documents" (the
+// pooled K/V of the chosen documents come first and the query's own K/V
+// after them; global RoPE moves the query start by k, keeping the order
+// background -> query -> generation); stage 3 of "EverMind Releases
+// Memory-Sparse Attention Code for Long-Context AI Models" (toolmesh.ai),
+// "Architectural Design and Inference".  The block form (token t of the
+// block is local token T - Tq + t and sees local tokens up to itself) is
+// this library's reading.
+//
+// Work item = one wave: (query b, KV head g, 16-row query tile, key split).
+// Rows of a tile are (token, head) pairs of one KV group, row = t*G + hh.
+// Per 16-key group:
+//   K   loaded straight from HBM in the MFMA A-operand layout (lane l: key
+//       l%16, dims 32s + 8(l/16) .. +8); local keys rotated in registers -
+//       the rotate-half partner of dim j < D/2 is in the same lane (block
+//       s + D/64), so RoPE needs no data exchange.  The phasor of (key, j)
+//       is one exact evaluation per 64-key block and pair (one per lane),
+//       times a table entry e^{i c w_j} for the key's offset c < 16;
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the rotated, scaled query
+//       split into bf16 head + remainder (two MFMAs per k-block);
+//       lane l then holds S[row l%16][keys 4(l/16) .. +4], which is exactly
+//       the A-operand layout of v_mfma_f32_16x16x16bf16_1k, so P feeds the
+//       PV product without any exchange;
+//   online softmax per row (exp2, log2(e) folded into q);
+//   V   loaded as 4 keys x D/16 dims per lane, written transposed into a
+//       per-wave LDS tile and read back as B-operands of the PV MFMAs.
+// The next group's K/V loads are issued before the current group is
+// computed.  Partials (m, l, acc) per (slot, row) go to the workspace; a
+// merge kernel combines the splits.  No barrier follows the one-time table
+// setup.
+#include "msa_internal.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace msa {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+constexpr int kAWaves = 4;          // independent work items per workgroup
+constexpr int kAMaxSplit = 4096;
+#ifndef MSA_ATT_SPLIT_MAX   // longest key split, a multiple of 64
+#define MSA_ATT_SPLIT_MAX 512
+#endif
+// Work items run KV head fastest, so the Hkv waves of one key range read
+// whole K/V rows together, and each query walks its splits from a different
+// start.  With split-fastest order and no rotation, capacities whose row
+// strides are multiples of large powers of two (4096 local tokens, 12288
+// memory rows) made concurrent waves collide in the memory system: 613 us
+// against 313 us for the same 64 x 4696 keys.
+#ifndef MSA_ATT_ORDER       // work item order: 0 split fastest, 1 KV head fastest
+#define MSA_ATT_ORDER 1
+#endif
+#ifndef MSA_ATT_ROTATE      // 1: rotate each query's split order by its index
+#define MSA_ATT_ROTATE 1
+#endif
+constexpr float kALog2e = 1.4426950408889634f;
+
+template <int D>
+struct AttnCfg {
+  static constexpr int KS = D / 32;   // 32-wide k-blocks of Q K^T
+  static constexpr int HS = KS / 2;   // k-blocks of the first rotate-half
+  static constexpr int NT = D / 16;   // 16-wide output column tiles
+  static constexpr int DB = D / 16;   // dims per lane in V staging
+  static constexpr int VTS = 16 + 4;  // LDS row (16 keys + pad) of the transposed V group, in bf16
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float amax4(const f32x4 &v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
+
+// bf16 number e (0..7) of a 16-byte vector
+__device__ __forceinline__ uint32_t bf16_at(const u32x4 &v, int e) {
+  const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+__device__ __forceinline__ uint32_t bf16_at(const u32x2 &v, int e) {
+  const uint32_t w = e < 2 ? v.x : v.y;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
+    const uint16_t *__restrict__ local_k, const uint16_t *__restrict__ local_v,
+    const int32_t *__restrict__ local_len, const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc,
+    float *__restrict__ part_ml, int B, int Tq, int Hq, int Hkv, int mem_cap, int local_cap, int n_mt, int n_split,
+    int split_len, int rps, float scale_log2, double log2_theta) {
+  using C = AttnCfg<D>;
+  constexpr int KS = C::KS, HS = C::HS, NT = C::NT, DB = C::DB, VTS = C::VTS, HALF = D / 2;
+  using VVec = typename std::conditional<DB == 8, u32x4, u32x2>::type;
+  __shared__ double omega[HALF];
+  __shared__ float2 step16[HALF];                          // e^{i 16 omega_j}
+  // rows padded so that the 16 key columns (F) and the 4 lane groups (zb)
+  // of one read fall in different LDS banks
+  constexpr int FS = HALF + 1;                             // F row stride
+  constexpr int ZS = HALF + HALF / 16;                     // zb row stride, entry j at j + j/16
+  __shared__ float2 ftab[16 * FS];                         // e^{i c omega_j}, c < 16
+  __shared__ float2 zb_all[kAWaves][4 * ZS];               // per wave: block phasors
+  __shared__ __align__(16) uint16_t vt_all[kAWaves][D * VTS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  int64_t item = (int64_t)blockIdx.x * kAWaves + wave;
+  const bool live = item < (int64_t)B * Hkv * n_mt * n_split;
+  if (!live) item = 0;                                     // decoded but never written
+#if MSA_ATT_ORDER == 1
+  // KV head fastest: the Hkv waves of one key range read whole K/V rows together
+  const int g = (int)(item % Hkv);
+  item /= Hkv;
+  const int split_i = (int)(item % n_split);
+  item /= n_split;
+  const int mt = (int)(item % n_mt);
+  const int b = (int)(item / n_mt);
+#else
+  const int split_i = (int)(item % n_split);
+  item /= n_split;
+  const int mt = (int)(item % n_mt);
+  item /= n_mt;
+  const int g = (int)(item % Hkv);
+  const int b = (int)(item / Hkv);
+#endif
+#if MSA_ATT_ROTATE
+  const int split = (int)((split_i + 5LL * b) % n_split);  // queries walk their key ranges out of step
+#else
+  const int split = split_i;
+#endif
+  const int G = Hq / Hkv;
+  uint16_t *vt = vt_all[wave];
+  float2 *zb = zb_all[wave];
+
+  const int M = max(0, min(mem_len[b], mem_cap));
+  const int T = max(0, min(local_len[b], local_cap));
+  const int o = pos_offset[b];
+  const int n_rows = Tq * G;
+  const int col = lane & 15, grp = lane >> 4;
+  // this lane's query row in the S layout and in the Q fragments
+  const int R = mt * 16 + col;
+  const bool row_ok = R < n_rows;
+  const int t_row = row_ok ? R / G : 0;
+  const int i_row = T - Tq + t_row;                        // local index of the row's token
+  // keys the tile can see: the memory, then local tokens up to its last token
+  const int t_last = min(Tq - 1, (mt * 16 + 15) / G);
+  const int key_end = M + max(0, min(T, T - Tq + t_last + 1));
+  const int k_begin = split * split_len;
+  const int k_end = min(key_end, k_begin + split_len);
+  const int64_t slot = (((int64_t)b * Hkv + g) * n_mt + mt) * n_split + split;
+  const bool active = live && k_begin < k_end;
+
+  // RoPE tables, only in workgroups with work (every thread reaches both
+  // barriers): w_j, e^{i c w_j} for c < 16 by products of e^{i w_j}, and
+  // e^{i 16 w_j}
+  if (__syncthreads_or(active)) {
+    if (threadIdx.x < HALF) {
+      const int j = threadIdx.x;
+      const double w = exp2(-(2.0 * j / D) * log2_theta);
+      omega[j] = w;
+      float c1, s1;
+      rope_phasor(1.0, w, &c1, &s1);
+      float2 z = make_float2(1.f, 0.f);
+      for (int c = 0; c < 16; ++c) {
+        ftab[c * FS + j] = z;
+        z = make_float2(z.x * c1 - z.y * s1, z.y * c1 + z.x * s1);
+      }
+      step16[j] = z;
+    }
+    __syncthreads();
+  }
+  if (!live) return;                                       // no barrier follows
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (active) {
+    // ---- rotated, scaled query as B-operand fragments (hi + lo bf16) ----
+    u32x4 qhi[KS], qlo[KS];
+    {
+      float x[KS][8];
+      const uint16_t *src = q + (((int64_t)b * Tq + t_row) * Hq + g * G + (row_ok ? R % G : 0)) * D + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 v = row_ok ? ld16(src + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+        float f[8];
+        Elt<uint16_t>::unpack(v, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[s][e] = f[e];
+      }
+#pragma unroll
+      for (int s = 0; s < HS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float c, sn;
+          rope_phasor((double)o + (double)i_row, omega[32 * s + 8 * grp + e], &c, &sn);
+          const float x1 = x[s][e], x2 = x[s + HS][e];
+          x[s][e] = (x1 * c - x2 * sn) * scale_log2;
+          x[s + HS][e] = (x2 * c + x1 * sn) * scale_log2;
+        }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = bf16_to_f32(f32_to_bf16(x[s][e]));
+          lo[e] = x[s][e] - hi[e];
+        }
+        qhi[s] = Elt<uint16_t>::pack(hi);
+        qlo[s] = Elt<uint16_t>::pack(lo);
+      }
+    }
+
+    const int64_t mem_row = 2LL * Hkv * D, loc_row = (int64_t)Hkv * D;
+    auto kaddr = [&](int k) -> const uint16_t * {
+      return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mem_row + (int64_t)g * D
+                   : local_k + ((int64_t)b * local_cap + (k - M)) * loc_row + (int64_t)g * D;
+    };
+    auto vaddr = [&](int k) -> const uint16_t * {
+      return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mem_row + loc_row + (int64_t)g * D
+                   : local_v + ((int64_t)b * local_cap + (k - M)) * loc_row + (int64_t)g * D;
+    };
+    // loads of the 16-key group at kb (keys past k_end read key k_end - 1;
+    // their scores are masked)
+    const int kq = lane & 3, db = lane >> 2;                // V staging: keys 4kq.., dims db*DB..
+    auto load = [&](int kb, u32x4 *kf, VVec *vv) {
+      const int kk = min(kb + col, k_end - 1);
+      const uint16_t *ks = kaddr(kk) + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[s] = ld16(ks + 32 * s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t *vs = vaddr(min(kb + 4 * kq + i, k_end - 1)) + db * DB;
+        vv[i] = *reinterpret_cast<const VVec *>(vs);
+      }
+    };
+
+    // RoPE of local keys.  Lane l holds key kb + col and the pairs
+    // j = 32 s + 8 grp + e (s < HS); its phasor e^{i (o + key - M) w_j} is
+    // zb[gi][j] * F[col][j], where zb[gi][j] = e^{i (o + kb0 - M + 16 gi) w_j}
+    // is evaluated exactly once per 64-key block (one pair per lane) and
+    // F[col][j] = e^{i col w_j} is a per-workgroup table.
+    auto block_phasors = [&](int kb0) {
+      if (lane < HALF) {
+        float c, sn;
+        rope_phasor((double)o + (double)(kb0 - M), omega[lane], &c, &sn);
+        float2 z = make_float2(c, sn);
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          zb[gi * ZS + lane + (lane >> 4)] = z;
+          const float2 w = step16[lane];
+          z = make_float2(z.x * w.x - z.y * w.y, z.y * w.x + z.x * w.y);
+        }
+      }
+    };
+    auto rotate = [&](int gi, int kb, u32x4 *kf) {
+      if (kb + col < M) return;                             // memory keys are used as stored
+#pragma unroll
+      for (int s = 0; s < HS; ++s) {
+        float a[8], c2[8], r1[8], r2[8];
+        Elt<uint16_t>::unpack(kf[s], a);
+        Elt<uint16_t>::unpack(kf[s + HS], c2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * s + 8 * grp + e;
+          const float2 zz = zb[gi * ZS + j + (j >> 4)], ff = ftab[col * FS + j];
+          const float zc = zz.x * ff.x - zz.y * ff.y, zs = zz.y * ff.x + zz.x * ff.y;
+          r1[e] = a[e] * zc - c2[e] * zs;
+          r2[e] = c2[e] * zc + a[e] * zs;
+        }
+        kf[s] = Elt<uint16_t>::pack(r1);
+        kf[s + HS] = Elt<uint16_t>::pack(r2);
+      }
+    };
+    // one 16-key group: rotation, S^T = K Q^T, online softmax, V transposed
+    // through LDS, O += P V
+    auto group = [&](int gi, int kb, u32x4 *kf, const VVec *vv) {
+      if (kb + 15 >= M) rotate(gi, kb, kf);
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kv8 = __builtin_bit_cast(bf16x8, kf[s]);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qhi[s]), sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qlo[s]), sc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < DB; ++e) {
+        u32x2 w;
+        w.x = bf16_at(vv[0], e) | (bf16_at(vv[1], e) << 16);
+        w.y = bf16_at(vv[2], e) | (bf16_at(vv[3], e) << 16);
+        *reinterpret_cast<u32x2 *>(vt + (db * DB + e) * VTS + 4 * kq) = w;
+      }
+      // mask: row must exist, key in range, local keys up to the row's token
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kb + 4 * grp + r;
+        const bool ok = row_ok && key < k_end && (key < M || key - M <= i_row);
+        sc[r] = ok ? sc[r] : -INFINITY;
+      }
+      float mt_ = amax4(sc);
+      mt_ = fmaxf(mt_, __shfl_xor(mt_, 16, 64));
+      mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, 64));
+      const float m_new = fmaxf(m_run, mt_);
+      const bool none = m_new == -INFINITY;
+      const float corr = none ? 1.f : exp2f(m_run - m_new);
+      float psum = 0.f;
+      s16x4 pa;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = none ? 0.f : exp2f(sc[r] - m_new);
+        psum += pr;
+        pa[r] = (short)f32_to_bf16(pr);
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+      // rows 4 grp + r of the accumulators take the factor of their row
+      float cr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r, 64);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] *= cr[r];
+        const u32x2 vb = *reinterpret_cast<const u32x2 *>(vt + (16 * nt + col) * VTS + 4 * grp);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, vb), acc[nt], 0, 0, 0);
+      }
+    };
+
+    u32x4 kfa[KS], kfb[KS];
+    VVec vva[4], vvb[4];
+    load(k_begin, kfa, vva);
+    for (int ks0 = k_begin; ks0 < k_end; ks0 += 64) {
+      if (ks0 + 63 >= M) block_phasors(ks0);
+      // four groups, buffers alternating; the last one loads the next block's first
+      load(ks0 + 16, kfb, vvb);
+      group(0, ks0, kfa, vva);
+      load(ks0 + 32, kfa, vva);
+      group(1, ks0 + 16, kfb, vvb);
+      load(ks0 + 48, kfb, vvb);
+      group(2, ks0 + 32, kfa, vva);
+      load(ks0 + 64, kfa, vva);
+      group(3, ks0 + 48, kfb, vvb);
+    }
+  }
+
+  // ---- partials: (m, l) from the S layout, acc from the O layout ----
+  if (grp == 0 && col < rps && row_ok) {
+    part_ml[2 * (slot * rps + col)] = m_run;
+    part_ml[2 * (slot * rps + col) + 1] = l_run;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * grp + r;
+    if (row < rps && mt * 16 + row < n_rows) {
+      float *dst = part_acc + (slot * rps + row) * D + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[nt][r];
+    }
+  }
+}
+
+// Combine the splits of one output row (b, t, h).  Wave 0 forms the
+// weights 2^(m_s - max m) in LDS and their l-weighted sum; then every thread
+// owns a float4 of the row and a stride of splits, with its loads issued
+// before the adds.
+template <int D>
+__global__ __launch_bounds__(256) void attend_merge_kernel(const float *__restrict__ part_acc,
+                                                          const float *__restrict__ part_ml, uint16_t *__restrict__ out,
+                                                          float *__restrict__ lse, int Tq, int Hq, int Hkv, int n_mt,
+                                                          int n_split, int rps) {
+  constexpr int NV = D / 4;               // float4 per output row
+  constexpr int NGRP = 256 / NV;          // split groups
+  __shared__ float w[kAMaxSplit];
+  __shared__ float s_m, s_l;
+  __shared__ float4 part[NGRP][NV];
+  const int64_t bth = blockIdx.x;                          // (b * Tq + t) * Hq + h
+  const int h = (int)(bth % Hq);
+  const int t = (int)((bth / Hq) % Tq);
+  const int b = (int)(bth / ((int64_t)Hq * Tq));
+  const int G = Hq / Hkv, g = h / G;
+  const int R = t * G + (h % G);
+  const int mt = R / 16, row = R % 16;
+  const int64_t base = ((((int64_t)b * Hkv + g) * n_mt + mt) * n_split) * rps + row;   // split s: base + s * rps
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    float m = -INFINITY;
+    for (int s = tid; s < n_split; s += 64) m = fmaxf(m, part_ml[2 * (base + (int64_t)s * rps)]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int s = tid; s < n_split; s += 64) {
+      const int64_t i = base + (int64_t)s * rps;
+      const float ms = part_ml[2 * i];
+      const float ws = ms == -INFINITY ? 0.f : exp2f(ms - m);
+      w[s] = ws;
+      l += ws * part_ml[2 * i + 1];
+    }
+    l = wave_sum(l);
+    if (tid == 0) { s_m = m; s_l = l; }
+  }
+  __syncthreads();
+  const int v = tid % NV, gq = tid / NV;
+  float4 a = {0.f, 0.f, 0.f, 0.f};
+  int s = gq;
+  for (; s + 3 * NGRP < n_split; s += 4 * NGRP) {
+    float4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      x[u] = reinterpret_cast<const float4 *>(part_acc + (base + (int64_t)(s + u * NGRP) * rps) * D)[v];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float ws = w[s + u * NGRP];
+      a.x += ws * x[u].x; a.y += ws * x[u].y; a.z += ws * x[u].z; a.w += ws * x[u].w;
+    }
+  }
+  for (; s < n_split; s += NGRP) {
+    const float ws = w[s];
+    const float4 x = reinterpret_cast<const float4 *>(part_acc + (base + (int64_t)s * rps) * D)[v];
+    a.x += ws * x.x; a.y += ws * x.y; a.z += ws * x.z; a.w += ws * x.w;
+  }
+  part[gq][v] = a;
+  __syncthreads();
+  if (tid < NV) {
+    float4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q2 = 0; q2 < NGRP; ++q2) {
+      r.x += part[q2][tid].x; r.y += part[q2][tid].y; r.z += part[q2][tid].z; r.w += part[q2][tid].w;
+    }
+    const float L = s_l;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    uint16_t *o = out + bth * D + 4 * tid;
+    *reinterpret_cast<uint2 *>(o) = make_uint2(pack_bf16x2(r.x * inv, r.y * inv), pack_bf16x2(r.z * inv, r.w * inv));
+  }
+  if (lse && tid == 0) lse[bth] = s_l > 0.f ? (s_m + log2f(s_l)) * 0.69314718055994531f : -INFINITY;
+}
+
+}  // namespace
+
+// Keys per split: enough work items (waves) to give every CU about 16, in
+// whole 64-key blocks, between 64 and 512 keys.  Sized from the capacities,
+// which the host knows; splits past a tile's visible keys exit at once.
+void attend_plan(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t mem_cap, int32_t local_cap,
+                 AttendPlan *p) {
+  const int G = hq / hkv;
+  p->n_mt = (q_tokens * G + 15) / 16;
+  p->rps = std::min(16, q_tokens * G);
+  const int64_t total = std::max<int64_t>(1, (int64_t)mem_cap + local_cap);
+  const int64_t tiles = (int64_t)batch * hkv * p->n_mt;
+  const int64_t want = (int64_t)device_info().n_cu * 16;
+  int64_t len = (total * tiles + want - 1) / want;
+  len = std::max<int64_t>(64, std::min<int64_t>(MSA_ATT_SPLIT_MAX, ((len + 63) / 64) * 64));
+  int64_t ns = (total + len - 1) / len;
+  if (ns > kAMaxSplit) {
+    ns = kAMaxSplit;
+    len = ((total + ns - 1) / ns + 63) / 64 * 64;
+    ns = (total + len - 1) / len;
+  }
+  p->split_len = (int)len;
+  p->n_split = (int)ns;
+}
+
+size_t attend_ws_layout(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t d, int32_t mem_cap,
+                        int32_t local_cap, void *base, float **part_acc, float **part_ml) {
+  AttendPlan p;
+  attend_plan(batch, q_tokens, hq, hkv, mem_cap, local_cap, &p);
+  const size_t rows = (size_t)batch * hkv * p.n_mt * p.n_split * p.rps;
+  const size_t o_ml = (sizeof(float) * rows * d + 255) & ~(size_t)255;
+  const size_t end = (o_ml + sizeof(float) * 2 * rows + 255) & ~(size_t)255;
+  if (base) {
+    *part_acc = reinterpret_cast<float *>(base);
+    *part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(base) + o_ml);
+  }
+  return end;
+}
+
+template <int D>
+static hipError_t launch_attend_t(const msa_attend_args &a, float *part_acc, float *part_ml, hipStream_t s) {
+  AttendPlan p;
+  attend_plan(a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap, a.local_cap, &p);
+  const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.0f / sqrtf((float)D);
+  const int64_t items = (int64_t)a.batch * a.n_kv_heads * p.n_mt * p.n_split;
+  const int64_t grid = (items + kAWaves - 1) / kAWaves;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a.prof_event_begin);
+  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a.prof_event_end);
+  hipError_t e = hipSuccess;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL((attend_kernel<D>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
+                     reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
+                     a.mem_len, reinterpret_cast<const uint16_t *>(a.local_k),
+                     reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset, part_acc, part_ml,
+                     a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap, a.local_cap, p.n_mt, p.n_split,
+                     p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.batch * a.q_tokens * a.n_q_heads;
+  hipLaunchKernelGGL((attend_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, s, part_acc, part_ml,
+                     reinterpret_cast<uint16_t *>(a.out), a.lse, a.q_tokens, a.n_q_heads, a.n_kv_heads, p.n_mt,
+                     p.n_split, p.rps);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const msa_attend_args &a, float *part_acc, float *part_ml, hipStream_t s) {
+  return a.head_dim == 128 ? launch_attend_t<128>(a, part_acc, part_ml, s)
+                           : launch_attend_t<64>(a, part_acc, part_ml, s);
+}
+
+}  // namespace msa

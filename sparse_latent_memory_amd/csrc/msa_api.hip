@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -226,10 +227,19 @@ int msa_route(const msa_route_args *a, void *stream) {
   return MSA_OK;
 }
 
+// bf16 decode runs the block-attention kernel with one query token (fp32
+// keeps the split-KV VALU kernel); the KV head count is not an argument
+// here, so the size covers every Hkv that divides Hq.
 size_t msa_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim, int32_t mem_cap,
                                   int32_t local_cap) {
   if (batch < 1 || n_q_heads < 1 || !dim_ok(head_dim) || mem_cap < 0 || local_cap < 0) return 0;
-  return decode_ws_layout(batch, n_q_heads, head_dim, mem_cap, local_cap, nullptr, nullptr, nullptr, nullptr);
+  size_t need = decode_ws_layout(batch, n_q_heads, head_dim, mem_cap, local_cap, nullptr, nullptr, nullptr, nullptr);
+  if ((int64_t)mem_cap + local_cap <= (1LL << 30))
+    for (int32_t hkv = 1; hkv <= n_q_heads; ++hkv)
+      if (n_q_heads % hkv == 0 && n_q_heads / hkv <= 16)
+        need = std::max(need, attend_ws_layout(batch, 1, n_q_heads, hkv, head_dim, mem_cap, local_cap, nullptr,
+                                               nullptr, nullptr));
+  return need;
 }
 
 int msa_sparse_decode(const msa_decode_args *a, void *stream) {
@@ -253,6 +263,40 @@ int msa_sparse_decode(const msa_decode_args *a, void *stream) {
       (a->local_v && !aligned16(a->local_v)))
     return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: K/V tensors must be 16-byte aligned");
   float *part_acc = nullptr, *part_ml = nullptr;
+  if (a->dtype == MSA_BF16 && aligned16(a->q) && aligned16(a->out)) {
+    // the block-attention kernel with one query token
+    msa_attend_args t = {};
+    t.dtype = a->dtype;
+    t.batch = a->batch;
+    t.q_tokens = 1;
+    t.n_q_heads = a->n_q_heads;
+    t.n_kv_heads = a->n_kv_heads;
+    t.head_dim = a->head_dim;
+    t.mem_cap = a->mem_cap;
+    t.local_cap = a->local_cap;
+    t.q = a->q;
+    t.mem_kv = a->mem_kv;
+    t.mem_len = a->mem_len;
+    t.local_k = a->local_k;
+    t.local_v = a->local_v;
+    t.local_len = a->local_len;
+    t.pos_offset = a->pos_offset;
+    t.rope_theta = a->rope_theta;
+    t.softmax_scale = a->softmax_scale;
+    t.out = a->out;
+    t.lse = a->lse;
+    t.prof_event_begin = a->prof_event_begin;
+    t.prof_event_end = a->prof_event_end;
+    const size_t need = attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap,
+                                         nullptr, nullptr, nullptr);
+    if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
+      return fail(MSA_ERR_WORKSPACE, "msa_sparse_decode: workspace needs %zu bytes (16-byte aligned), got %zu",
+                  need, a->workspace ? a->workspace_bytes : (size_t)0);
+    attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap, a->workspace,
+                     &part_acc, &part_ml);
+    hipError_t e = launch_attend(t, part_acc, part_ml, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_decode launch");
+  }
   int32_t n_split = 0;
   const size_t need =
       decode_ws_layout(a->batch, a->n_q_heads, a->head_dim, a->mem_cap, a->local_cap, nullptr, nullptr, nullptr,
@@ -264,6 +308,50 @@ int msa_sparse_decode(const msa_decode_args *a, void *stream) {
                    &part_ml, &n_split);
   hipError_t e = launch_decode(*a, part_acc, part_ml, n_split, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_decode launch");
+}
+
+size_t msa_attend_workspace_bytes(int32_t batch, int32_t q_tokens, int32_t n_q_heads, int32_t n_kv_heads,
+                                  int32_t head_dim, int32_t mem_cap, int32_t local_cap) {
+  if (batch < 1 || q_tokens < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0 ||
+      n_q_heads / n_kv_heads > 16 || !dim_ok(head_dim) || mem_cap < 0 || local_cap < 0 ||
+      (int64_t)mem_cap + local_cap > (1LL << 30))
+    return 0;
+  return attend_ws_layout(batch, q_tokens, n_q_heads, n_kv_heads, head_dim, mem_cap, local_cap, nullptr, nullptr,
+                          nullptr);
+}
+
+int msa_sparse_attend(const msa_attend_args *a, void *stream) {
+  if (!a) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attend: args is NULL");
+  if (!dtype_ok(a->dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attend: bad dtype %d", a->dtype);
+  if (a->dtype != MSA_BF16) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attend: bf16 only");
+  if (a->batch < 1 || a->q_tokens < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1 || a->mem_cap < 0 ||
+      a->local_cap < 0 || !(a->rope_theta > 0.0))
+    return fail(MSA_ERR_INVALID_ARG,
+                "msa_sparse_attend: need batch, q_tokens, heads >= 1, caps >= 0, rope_theta > 0");
+  if (a->n_q_heads % a->n_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attend: n_q_heads (%d) not a multiple of n_kv_heads (%d)",
+                a->n_q_heads, a->n_kv_heads);
+  if (a->n_q_heads / a->n_kv_heads > 16)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attend: more than 16 query heads per KV head");
+  if (!dim_ok(a->head_dim)) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attend: head_dim must be 64 or 128");
+  if ((int64_t)a->mem_cap + a->local_cap > (1LL << 30))
+    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_attend: context capacity too large");
+  if (!a->q || !a->mem_len || !a->local_len || !a->pos_offset || !a->out || (a->mem_cap > 0 && !a->mem_kv) ||
+      (a->local_cap > 0 && (!a->local_k || !a->local_v)))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attend: NULL pointer");
+  if (!aligned16(a->q) || !aligned16(a->out) || (a->mem_kv && !aligned16(a->mem_kv)) ||
+      (a->local_k && !aligned16(a->local_k)) || (a->local_v && !aligned16(a->local_v)))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attend: q, out and K/V tensors must be 16-byte aligned");
+  const size_t need = attend_ws_layout(a->batch, a->q_tokens, a->n_q_heads, a->n_kv_heads, a->head_dim,
+                                       a->mem_cap, a->local_cap, nullptr, nullptr, nullptr);
+  if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
+    return fail(MSA_ERR_WORKSPACE, "msa_sparse_attend: workspace needs %zu bytes (16-byte aligned), got %zu",
+                need, a->workspace ? a->workspace_bytes : (size_t)0);
+  float *part_acc = nullptr, *part_ml = nullptr;
+  attend_ws_layout(a->batch, a->q_tokens, a->n_q_heads, a->n_kv_heads, a->head_dim, a->mem_cap, a->local_cap,
+                   a->workspace, &part_acc, &part_ml);
+  hipError_t e = launch_attend(*a, part_acc, part_ml, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_attend launch");
 }
 
 }  // extern "C"

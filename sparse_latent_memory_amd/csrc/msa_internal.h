@@ -127,4 +127,17 @@ size_t decode_ws_layout(int32_t batch, int32_t hq, int32_t d, int32_t mem_cap, i
 hipError_t launch_decode(const msa_decode_args &a, float *part_acc, float *part_ml, int32_t n_split,
                          hipStream_t s);
 
+// Block attention: work items (query, KV head, 16-row query tile, key split).
+struct AttendPlan {
+  int32_t n_mt;            // 16-row tiles of (token, head) rows per KV head
+  int32_t rps;             // rows kept per partial slot: min(16, Tq * G)
+  int32_t split_len;       // keys per split, a multiple of 64
+  int32_t n_split;
+};
+void attend_plan(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t mem_cap, int32_t local_cap,
+                 AttendPlan *p);
+size_t attend_ws_layout(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t d, int32_t mem_cap,
+                        int32_t local_cap, void *base, float **part_acc, float **part_ml);
+hipError_t launch_attend(const msa_attend_args &a, float *part_acc, float *part_ml, hipStream_t s);
+
 }  // namespace msa

@@ -42,7 +42,7 @@ def test_version():
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
 def test_ctypes_struct_layout_matches_c(tmp_path):
     structs = {"msa_pool_args": _lib.PoolArgs, "msa_route_args": _lib.RouteArgs,
-               "msa_decode_args": _lib.DecodeArgs}
+               "msa_decode_args": _lib.DecodeArgs, "msa_attend_args": _lib.AttendArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -206,3 +206,43 @@ def test_decode_rejects_bad_arguments(kw, code):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load(str(tmp_path / "missing" / "libmsa.so"))
+
+
+def _attend_args(**kw):
+    a = _lib.AttendArgs(dtype=1, batch=1, q_tokens=4, n_q_heads=32, n_kv_heads=8, head_dim=128, mem_cap=128,
+                        local_cap=64, q=_p(), mem_kv=_p(), mem_len=_p(), local_k=_p(), local_v=_p(), local_len=_p(),
+                        pos_offset=_p(), rope_theta=1e6, softmax_scale=0.0, out=_p(), lse=None, workspace=_p(),
+                        workspace_bytes=16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 0}, _lib.MSA_ERR_UNSUPPORTED),                   # fp32: bf16 only
+    ({"dtype": 5}, _lib.MSA_ERR_INVALID_ARG),
+    ({"q_tokens": 0}, _lib.MSA_ERR_INVALID_ARG),
+    ({"n_q_heads": 30}, _lib.MSA_ERR_INVALID_ARG),              # not a multiple of Hkv
+    ({"n_q_heads": 136}, _lib.MSA_ERR_UNSUPPORTED),             # 17 query heads per KV head
+    ({"head_dim": 80}, _lib.MSA_ERR_UNSUPPORTED),
+    ({"mem_kv": None}, _lib.MSA_ERR_INVALID_ARG),               # mem_cap > 0 needs memory
+    ({"local_k": None}, _lib.MSA_ERR_INVALID_ARG),
+    ({"rope_theta": 0.0}, _lib.MSA_ERR_INVALID_ARG),
+    ({"q": ctypes.c_void_p(_B + 8)}, _lib.MSA_ERR_INVALID_ARG),  # misaligned query
+    ({}, _lib.MSA_ERR_WORKSPACE),
+])
+def test_attend_rejects_bad_arguments(kw, code):
+    lib = _lib.load()
+    a = _attend_args(**kw)
+    assert lib.msa_sparse_attend(ctypes.byref(a), None) == code, lib.msa_last_error()
+
+
+def test_attend_workspace_size():
+    lib = _lib.load()
+    assert lib.msa_attend_workspace_bytes(1, 256, 32, 8, 128, 256, 2048) > 0
+    assert lib.msa_attend_workspace_bytes(64, 1, 32, 8, 128, 12288, 4096) > 0
+    assert lib.msa_attend_workspace_bytes(1, 0, 32, 8, 128, 256, 2048) == 0      # no tokens
+    assert lib.msa_attend_workspace_bytes(1, 4, 34, 8, 128, 256, 2048) == 0      # Hq not a multiple of Hkv
+    assert lib.msa_attend_workspace_bytes(1, 4, 32, 8, 96, 256, 2048) == 0       # head dim
+

@@ -396,6 +396,99 @@ def test_decode_local_only_is_offset_invariant():
 
 
 # ==========================================================================
+# stage 3 for a block of query tokens (prefill through the sparse context)
+# ==========================================================================
+
+def _attend_check(b, tq, hq, hkv, d, mem_cap, loc_cap, mem_len, loc_len, pos, what, mem_scale=1.0, seed=0,
+                  theta=THETA):
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, b, tq, hq, d, dtype=torch.bfloat16)
+    mem = None
+    if mem_cap:
+        mem = torch.randn(b, mem_cap, 2, hkv, d, generator=g)
+        mem[:, :, 0] *= mem_scale
+        mem = mem.to(torch.bfloat16)
+    lk = _randn(g, b, loc_cap, hkv, d, dtype=torch.bfloat16)
+    lv = _randn(g, b, loc_cap, hkv, d, dtype=torch.bfloat16)
+    i32 = lambda x: torch.as_tensor(np.asarray(x, dtype=np.int32)).to(DEV)  # noqa: E731
+    out, lse = msa.sparse_attend(_dev(q), None if mem is None else _dev(mem), i32(mem_len), _dev(lk), _dev(lv),
+                                 i32(loc_len), i32(pos), theta)
+    torch.cuda.synchronize()
+    mem_np = np64(mem) if mem is not None else np.zeros((b, 0, 2, hkv, d))
+    ro, rl = oracle.attend(np64(q), mem_np, mem_len, np64(lk), np64(lv), loc_len, pos, theta, None, "bf16")
+    check_decode(np64(out).reshape(b * tq, hq, d), ro.reshape(b * tq, hq, d), torch.bfloat16, what)
+    gl = np64(lse)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(gl), fin), what
+    assert np.all(np.abs(gl[fin] - rl[fin]) <= 2e-2), f"{what}: lse off by {np.abs(gl[fin] - rl[fin]).max():.3g}"
+    return np64(out), gl, q, mem, lk, lv
+
+
+@pytest.mark.parametrize("mem_scale", [1.0, 8.0])
+def test_attend_one_token_at_the_100m_decode_shape(mem_scale):
+    """One query token: the decode step over 128 memory rows and 4096 local
+    tokens, checked against the oracle (and so against msa_sparse_decode's
+    definition)."""
+    _say(f"attend: Tq=1, 32/8 x 128, memory 128 rows (K x{mem_scale}), local 4096")
+    _attend_check(1, 1, 32, 8, 128, 128, 4096, [128], [4096], [16], "attend decode shape", mem_scale=mem_scale,
+                  seed=int(mem_scale))
+
+
+def test_attend_prefill_routing_layer_shape():
+    """256 prefill tokens (the last 256 of 2048 local tokens) over ~170
+    memory rows, GQA 32/8 x 128: 64 query tiles per KV head, causal."""
+    _say("attend: Tq=256 prefill, 32/8 x 128, memory 170 rows, local 2048")
+    _attend_check(1, 256, 32, 8, 128, 256, 2048, [170], [2048], [16], "prefill", mem_scale=8.0, seed=5)
+
+
+def test_attend_interleave_batch_shape():
+    _say("attend: 64 queries x 1 token, memory 600 rows, local 1024")
+    _attend_check(64, 1, 32, 8, 128, 700, 1024, list(range(540, 604)), [1024] * 64, [8] * 64, "batch 64",
+                  mem_scale=4.0, seed=6)
+
+
+@pytest.mark.parametrize("hq,hkv,d,tq", [(32, 8, 128, 5), (16, 2, 64, 7), (16, 1, 64, 3), (8, 8, 128, 20),
+                                         (4, 2, 64, 33)])
+def test_attend_ragged_batch_and_head_shapes(hq, hkv, d, tq):
+    """Ragged memory and local lengths (one query with fewer local tokens
+    than query tokens, one without memory), groups of 1 to 16 query heads,
+    head dims 64 and 128, token counts that leave a partial last tile."""
+    _say(f"attend: ragged batch of 4, Hq={hq} Hkv={hkv} D={d} Tq={tq}")
+    _attend_check(4, tq, hq, hkv, d, 150, 300, [0, 37, 150, 64], [300, tq, 2, 129], [0, 9, 1000, 16],
+                  f"ragged {hq}/{hkv}x{d} Tq{tq}", mem_scale=4.0, seed=hq + d + tq)
+
+
+def test_attend_empty_contexts_and_large_offset():
+    _say("attend: no keys at all / memory only / offset 1e6")
+    out, lse, *_ = _attend_check(3, 2, 8, 2, 128, 16, 8, [0, 16, 5], [0, 0, 8], [0, 4, 1_000_000],
+                                 "empty and offset", mem_scale=4.0)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    _say("attend: no memory buffer (capacity 0)")
+    _attend_check(1, 3, 8, 2, 64, 0, 70, [0], [70], [3], "no memory")
+
+
+def test_attend_is_causal_on_the_gpu():
+    """Changing the last local token (the last query token's own key and
+    value) leaves every earlier query token's output bit for bit."""
+    g = torch.Generator().manual_seed(12)
+    tq, t = 6, 200
+    q = _randn(g, 1, tq, 32, 128, dtype=torch.bfloat16).to(DEV)
+    mem = _randn(g, 1, 40, 2, 8, 128, dtype=torch.bfloat16).to(DEV)
+    lk = _randn(g, 1, t, 8, 128, dtype=torch.bfloat16).to(DEV)
+    lv = _randn(g, 1, t, 8, 128, dtype=torch.bfloat16).to(DEV)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=DEV)  # noqa: E731
+    _say("attend: causality, last local token perturbed")
+    a, _ = msa.sparse_attend(q, mem, i32([40]), lk, lv, i32([t]), i32([16]), THETA)
+    lk2, lv2 = lk.clone(), lv.clone()
+    lk2[0, -1] += 1.0
+    lv2[0, -1] -= 1.0
+    b, _ = msa.sparse_attend(q, mem, i32([40]), lk2, lv2, i32([t]), i32([16]), THETA)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0, :tq - 1], b[0, :tq - 1])
+    assert not torch.equal(a[0, tq - 1], b[0, tq - 1])
+
+
+# ==========================================================================
 # context assembly (gather)
 # ==========================================================================
 
