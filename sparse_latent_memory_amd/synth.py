@@ -245,6 +245,13 @@ def decode_queries(cfg, step=0, device="cpu"):
     return x.to(cfg.torch_dtype)
 
 
+def prefill_queries(cfg, step=0, device="cpu"):
+    """q [B, Tq, Hq, D] (before RoPE) for a block of query tokens, in
+    storage dtype."""
+    x = _normal_rows(cfg.cid, T_Q, cfg.batch * cfg.q_tokens, (cfg.n_q_heads, cfg.head_dim), device, step + 1000)
+    return x.reshape(cfg.batch, cfg.q_tokens, cfg.n_q_heads, cfg.head_dim).to(cfg.torch_dtype)
+
+
 def local_context(cfg, cap=None, device="cpu"):
     """Local K (before RoPE) and V [B, T_cap, Hkv, D]; every query holds
     cfg.local_len tokens."""
