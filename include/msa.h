@@ -82,6 +82,13 @@ typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
  * Attention) - An Open-Source Answer to AI's Memory Bottleneck").
  * Only K is rotated; V and Kr are averaged as given.  Accumulation is fp32,
  * the result is rounded to nearest-even into `dtype`.
+ * Either output may be pinned host memory (hipHostMalloc, or torch's
+ * pin_memory) instead of device memory: the kernel then writes the pooled
+ * rows through the buffer's device mapping, straight over the host link -
+ * this is how a large bank streams its pooled K/V into the host-resident
+ * content tier while the next batch is encoded.  Pageable host memory and
+ * another device's memory are rejected (MSA_ERR_INVALID_ARG) before any
+ * launch.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t dtype;            /* msa_dtype of k, v, kr and both outputs       */
@@ -100,8 +107,9 @@ typedef struct {
   const void *k;            /* device [n_tokens, Hkv, D], K before RoPE     */
   const void *v;            /* device [n_tokens, Hkv, D]                    */
   const void *kr;           /* device [n_tokens, Hr, dr]                    */
-  void *kv_pooled;          /* device out [n_pool, 2, Hkv, D]: K_bar, V_bar */
-  void *kr_pooled;          /* device out [n_pool, Hr, dr]                  */
+  void *kv_pooled;          /* out [n_pool, 2, Hkv, D]: K_bar, V_bar; device
+                               or pinned host memory                        */
+  void *kr_pooled;          /* out [n_pool, Hr, dr]; device or pinned host  */
 } msa_pool_args;
 
 int msa_pool_encode(const msa_pool_args *args, void *stream);

@@ -125,6 +125,31 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _dptr(t, name, pinned_ok=False):
+    """Pointer to a dense device tensor (or, where the library allows it, a
+    pinned CPU tensor); anything else is refused here, before it could reach
+    a kernel as an address the GPU cannot map."""
+    if t is None:
+        return None
+    if not (t.is_cuda or (pinned_ok and t.device.type == "cpu" and t.is_pinned())):
+        raise ValueError(f"{name} must be a {'CUDA or pinned CPU' if pinned_ok else 'CUDA'} tensor, "
+                         f"got one on {t.device}{' (not pinned)' if t.device.type == 'cpu' else ''}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _ptr(t)
+
+
+def _hptr(t, name, pinned=False):
+    """Pointer to a dense CPU tensor (pinned where the library maps it)."""
+    if t is None:
+        return None
+    if t.device.type != "cpu" or (pinned and not t.is_pinned()):
+        raise ValueError(f"{name} must be a {'pinned ' if pinned else ''}CPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _ptr(t)
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -145,7 +170,9 @@ def dtype_code(dtype):
 def pool_encode(k, v, kr, doc_tok_off, doc_pool_off, pool_size, rope_theta, n_pool,
                 kv_pooled=None, kr_pooled=None, stream=None):
     """msa_pool_encode.  k, v: [T, Hkv, D]; kr: [T, Hr, dr] (device, same
-    dtype); offsets: int64 device [n_docs+1].  Returns (kv_pooled, kr_pooled)."""
+    dtype); offsets: int64 device [n_docs+1].  The outputs may be device
+    tensors or pinned CPU tensors (written straight over the host link).
+    Returns (kv_pooled, kr_pooled)."""
     n_tok, hkv, d = k.shape
     _, hr, dr = kr.shape
     if kv_pooled is None:
@@ -154,8 +181,10 @@ def pool_encode(k, v, kr, doc_tok_off, doc_pool_off, pool_size, rope_theta, n_po
         kr_pooled = torch.empty((n_pool, hr, dr), dtype=k.dtype, device=k.device)
     a = PoolArgs(dtype=dtype_code(k.dtype), n_docs=doc_tok_off.numel() - 1, n_tokens=n_tok, n_pool=n_pool,
                  pool_size=pool_size, n_kv_heads=hkv, head_dim=d, n_router_heads=hr, router_dim=dr,
-                 rope_theta=float(rope_theta), doc_tok_off=_ptr(doc_tok_off), doc_pool_off=_ptr(doc_pool_off),
-                 k=_ptr(k), v=_ptr(v), kr=_ptr(kr), kv_pooled=_ptr(kv_pooled), kr_pooled=_ptr(kr_pooled))
+                 rope_theta=float(rope_theta), doc_tok_off=_dptr(doc_tok_off, "doc_tok_off"),
+                 doc_pool_off=_dptr(doc_pool_off, "doc_pool_off"), k=_dptr(k, "k"), v=_dptr(v, "v"),
+                 kr=_dptr(kr, "kr"), kv_pooled=_dptr(kv_pooled, "kv_pooled", pinned_ok=True),
+                 kr_pooled=_dptr(kr_pooled, "kr_pooled", pinned_ok=True))
     _check(load().msa_pool_encode(ctypes.byref(a), _stream(stream)))
     return kv_pooled, kr_pooled
 
@@ -219,24 +248,25 @@ def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, to
         nbytes = route_workspace_bytes(qr.dtype, b, tq, hr, dr, n_docs, n_pool, top_k)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     a = RouteArgs(dtype=dtype_code(qr.dtype), batch=b, q_tokens=tq, n_router_heads=hr, router_dim=dr,
-                  top_k=top_k, n_docs=n_docs, n_pool=n_pool, qr=_ptr(qr), kr_pooled=_ptr(kr_pooled),
-                  doc_pool_off=_ptr(doc_pool_off), doc_scores=_ptr(doc_scores), topk_idx=_ptr(topk_idx),
-                  topk_score=_ptr(topk_score), workspace=_ptr(workspace), workspace_bytes=workspace.numel())
+                  top_k=top_k, n_docs=n_docs, n_pool=n_pool, qr=_dptr(qr, "qr"), kr_pooled=_dptr(kr_pooled, "kr_pooled"),
+                  doc_pool_off=_dptr(doc_pool_off, "doc_pool_off"), doc_scores=_dptr(doc_scores, "doc_scores"),
+                  topk_idx=_dptr(topk_idx, "topk_idx"), topk_score=_dptr(topk_score, "topk_score"),
+                  workspace=_dptr(workspace, "workspace"), workspace_bytes=workspace.numel())
     if assembly is not None:
         asm = assembly
-        a.host_kv = _ptr(asm.host_kv)
-        a.host_doc_pool_off = _ptr(asm.host_doc_pool_off)
+        a.host_kv = _hptr(asm.host_kv, "host_kv", pinned=asm.mode == "kernel")
+        a.host_doc_pool_off = _hptr(asm.host_doc_pool_off, "host_doc_pool_off")
         a.kv_dtype = dtype_code(asm.host_kv.dtype)
         a.n_kv_heads = asm.host_kv.shape[2]
         a.head_dim = asm.host_kv.shape[3]
         a.mem_cap = asm.mem_kv.shape[1]
         a.append = 1 if asm.append else 0
         a.gather_mode = MSA_GATHER_KERNEL if asm.mode == "kernel" else MSA_GATHER_COPIES
-        a.mem_kv = _ptr(asm.mem_kv)
-        a.mem_len = _ptr(asm.mem_len)
-        a.host_topk_idx = _ptr(asm.host_topk_idx)
-        a.host_mem_len = _ptr(asm.host_mem_len)
-        a.host_mem_docs = _ptr(asm.host_mem_docs)
+        a.mem_kv = _dptr(asm.mem_kv, "mem_kv")
+        a.mem_len = _dptr(asm.mem_len, "mem_len")
+        a.host_topk_idx = _hptr(asm.host_topk_idx, "host_topk_idx")
+        a.host_mem_len = _hptr(asm.host_mem_len, "host_mem_len")
+        a.host_mem_docs = _hptr(asm.host_mem_docs, "host_mem_docs")
         cs = asm.copy_stream if asm.copy_stream is not None else stream
         a.copy_stream = _stream(cs)
     if prof_events is not None:
@@ -271,10 +301,12 @@ def sparse_decode(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, r
         nbytes = decode_workspace_bytes(b, hq, d, m_cap, t_cap)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     a = DecodeArgs(dtype=dtype_code(q.dtype), batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, mem_cap=m_cap,
-                   local_cap=t_cap, q=_ptr(q), mem_kv=_ptr(mem_kv), mem_len=_ptr(mem_len), local_k=_ptr(local_k),
-                   local_v=_ptr(local_v), local_len=_ptr(local_len), pos_offset=_ptr(pos_offset),
-                   rope_theta=float(rope_theta), softmax_scale=float(softmax_scale), out=_ptr(out),
-                   lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=workspace.numel())
+                   local_cap=t_cap, q=_dptr(q, "q"), mem_kv=_dptr(mem_kv, "mem_kv"), mem_len=_dptr(mem_len, "mem_len"),
+                   local_k=_dptr(local_k, "local_k"), local_v=_dptr(local_v, "local_v"),
+                   local_len=_dptr(local_len, "local_len"), pos_offset=_dptr(pos_offset, "pos_offset"),
+                   rope_theta=float(rope_theta), softmax_scale=float(softmax_scale), out=_dptr(out, "out"),
+                   lse=_dptr(lse, "lse"), workspace=_dptr(workspace, "workspace"),
+                   workspace_bytes=workspace.numel())
     if prof_events is not None:
         a.prof_event_begin, a.prof_event_end = prof_events
     _check(load().msa_sparse_decode(ctypes.byref(a), _stream(stream)))
@@ -305,10 +337,12 @@ def sparse_attend(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, r
         nbytes = attend_workspace_bytes(b, tq, hq, hkv, d, m_cap, t_cap)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     a = AttendArgs(dtype=dtype_code(q.dtype), batch=b, q_tokens=tq, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
-                   mem_cap=m_cap, local_cap=t_cap, q=_ptr(q), mem_kv=_ptr(mem_kv), mem_len=_ptr(mem_len),
-                   local_k=_ptr(local_k), local_v=_ptr(local_v), local_len=_ptr(local_len),
-                   pos_offset=_ptr(pos_offset), rope_theta=float(rope_theta), softmax_scale=float(softmax_scale),
-                   out=_ptr(out), lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=workspace.numel())
+                   mem_cap=m_cap, local_cap=t_cap, q=_dptr(q, "q"), mem_kv=_dptr(mem_kv, "mem_kv"),
+                   mem_len=_dptr(mem_len, "mem_len"), local_k=_dptr(local_k, "local_k"),
+                   local_v=_dptr(local_v, "local_v"), local_len=_dptr(local_len, "local_len"),
+                   pos_offset=_dptr(pos_offset, "pos_offset"), rope_theta=float(rope_theta),
+                   softmax_scale=float(softmax_scale), out=_dptr(out, "out"), lse=_dptr(lse, "lse"),
+                   workspace=_dptr(workspace, "workspace"), workspace_bytes=workspace.numel())
     if prof_events is not None:
         a.prof_event_begin, a.prof_event_end = prof_events
     _check(load().msa_sparse_attend(ctypes.byref(a), _stream(stream)))

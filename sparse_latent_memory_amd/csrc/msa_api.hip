@@ -109,7 +109,38 @@ int msa_pool_encode(const msa_pool_args *a, void *stream) {
   if (!aligned16(a->k) || !aligned16(a->v) || !aligned16(a->kr) || !aligned16(a->kv_pooled) ||
       !aligned16(a->kr_pooled))
     return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: tensors must be 16-byte aligned");
-  hipError_t e = launch_pool(*a, reinterpret_cast<hipStream_t>(stream));
+  // an output in pinned host memory (the content tier) is written through its
+  // device mapping, straight over the host link.  Anything else that is not
+  // this device's memory (pageable host memory reports "unregistered") is
+  // refused before any launch: the kernel could not store to it.
+  msa_pool_args t = *a;
+  void *outs[2] = {t.kv_pooled, t.kr_pooled};
+  int cur_dev = -1;
+  if (hipError_t ge = hipGetDevice(&cur_dev); ge != hipSuccess) return hip_fail(ge, "msa_pool_encode: hipGetDevice");
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t attr;
+    const bool known = hipPointerGetAttributes(&attr, outs[i]) == hipSuccess;
+    if (!known) (void)hipGetLastError();
+    const bool on_device = known && attr.type == hipMemoryTypeDevice && attr.device == cur_dev;
+    const bool pinned = known && attr.type == hipMemoryTypeHost;
+    if (!on_device && !pinned)
+      return fail(MSA_ERR_INVALID_ARG,
+                  "msa_pool_encode: %s must be device memory (of the current device) or pinned host memory",
+                  i ? "kr_pooled" : "kv_pooled");
+    if (pinned) {
+      void *dev = nullptr;
+      if (hipHostGetDevicePointer(&dev, outs[i], 0) != hipSuccess || !dev || !aligned16(dev)) {
+        (void)hipGetLastError();
+        return fail(MSA_ERR_INVALID_ARG,
+                    "msa_pool_encode: %s must be device memory or pinned host memory (no device mapping)",
+                    i ? "kr_pooled" : "kv_pooled");
+      }
+      outs[i] = dev;
+    }
+  }
+  t.kv_pooled = outs[0];
+  t.kr_pooled = outs[1];
+  hipError_t e = launch_pool(t, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_pool_encode launch");
 }
 

@@ -246,3 +246,32 @@ def test_attend_workspace_size():
     assert lib.msa_attend_workspace_bytes(1, 4, 34, 8, 128, 256, 2048) == 0      # Hq not a multiple of Hkv
     assert lib.msa_attend_workspace_bytes(1, 4, 32, 8, 96, 256, 2048) == 0       # head dim
 
+
+
+def test_binding_refuses_host_tensors_for_device_arguments():
+    """A CPU tensor passed where the library takes device memory is refused
+    by the binding before any call, with the argument named; pooled outputs
+    may be pinned CPU tensors, but not pageable ones."""
+    import sparse_latent_memory_amd as msa
+    f, i32, i64 = torch.float32, torch.int32, torch.int64
+    k = torch.zeros(8, 1, 64, dtype=f)
+    off = torch.tensor([0, 8], dtype=i64)
+    with pytest.raises(ValueError, match="doc_tok_off must be a CUDA"):
+        msa.pool_encode(k, k, k, off, torch.tensor([0, 1], dtype=i64), 8, 1e4, 1)
+    with pytest.raises(ValueError, match="qr must be a CUDA"):
+        msa.route(torch.zeros(1, 1, 1, 64, dtype=f), k, off, 1)
+    lens = torch.ones(1, dtype=i32)
+    with pytest.raises(ValueError, match="q must be a CUDA"):
+        msa.sparse_decode(torch.zeros(1, 1, 64, dtype=f), None, None, torch.zeros(1, 4, 1, 64, dtype=f),
+                          torch.zeros(1, 4, 1, 64, dtype=f), lens, lens, 1e4)
+    with pytest.raises(ValueError, match="q must be a CUDA"):
+        msa.sparse_attend(torch.zeros(1, 1, 1, 64, dtype=torch.bfloat16), None, None,
+                          torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16), torch.zeros(1, 4, 1, 64,
+                          dtype=torch.bfloat16), lens, lens, 1e4)
+    with pytest.raises(ValueError, match="must be contiguous"):
+        _lib._hptr(torch.zeros(4, 4).t(), "x")
+    with pytest.raises(ValueError, match="not pinned"):
+        _lib._dptr(torch.zeros(4), "kv_pooled", pinned_ok=True)
+    with pytest.raises(ValueError, match="pinned CPU tensor"):
+        _lib._hptr(torch.zeros(4), "host_kv", pinned=True)
+    assert _lib._hptr(torch.zeros(4), "host_doc_pool_off") is not None

@@ -3,6 +3,8 @@ seeded inputs, through the C ABI (ctypes binding).  Stage-wise tests feed
 the oracle and the library the same stored inputs; the chain tests run
 pool -> route -> gather -> decode end to end."""
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -117,6 +119,43 @@ def test_pool_routing_layer_config_sampled():
         check_pool(np64(kv_g[r0:r1, 0]), kb, torch.bfloat16, f"doc {d} K_bar")
         check_pool(np64(kv_g[r0:r1, 1]), vb, torch.bfloat16, f"doc {d} V_bar")
         check_pool(np64(kr_g[r0:r1]), rb, torch.bfloat16, f"doc {d} Kr_bar")
+
+
+def test_pool_into_pinned_host_tier():
+    """Pooled K/V written straight into pinned host memory (the content
+    tier) equal, bit for bit, the same call into device memory; a batch is
+    written at its row offset inside a larger host tier."""
+    cfg = synth.config(2, n_docs=96)
+    bank = synth.raw_bank(cfg, device=DEV)
+    lens = bank["lens"]
+    off = _dev(synth.row_offsets(lens, cfg.pool))
+    n_pool = int(synth.row_offsets(lens, cfg.pool)[-1])
+    _say(f"pool: {len(lens)} docs into pinned host memory ({n_pool} rows)")
+    kv_d, kr_d = msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], off, cfg.pool,
+                                 cfg.rope_theta, n_pool)
+    tier = torch.zeros((n_pool + 50, 2, 8, 128), dtype=torch.bfloat16, pin_memory=True)
+    kr_h = torch.zeros((n_pool, 8, 128), dtype=torch.bfloat16, pin_memory=True)
+    msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], off, cfg.pool, cfg.rope_theta,
+                    n_pool, tier[50:], kr_h)
+    torch.cuda.synchronize()
+    assert torch.equal(tier[50:].view(torch.int16), kv_d.cpu().view(torch.int16))
+    assert torch.equal(kr_h.view(torch.int16), kr_d.cpu().view(torch.int16))
+    assert not tier[:50].view(torch.int16).any()
+    pageable = torch.zeros(tuple(tier[50:].shape), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="not pinned"):
+        msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], off, cfg.pool, cfg.rope_theta,
+                        n_pool, pageable, kr_h)
+    # the library refuses pageable memory by itself too (straight through the C ABI)
+    a = _lib.PoolArgs(dtype=_lib.MSA_BF16, n_docs=len(lens), n_tokens=bank["k"].shape[0], n_pool=n_pool,
+                      pool_size=cfg.pool, n_kv_heads=8, head_dim=128, n_router_heads=8, router_dim=128,
+                      rope_theta=cfg.rope_theta, doc_tok_off=_lib._ptr(bank["doc_tok_off"]),
+                      doc_pool_off=_lib._ptr(off), k=_lib._ptr(bank["k"]), v=_lib._ptr(bank["v"]),
+                      kr=_lib._ptr(bank["kr"]), kv_pooled=_lib._ptr(pageable), kr_pooled=_lib._ptr(kr_h))
+    lib = _lib.load()
+    assert lib.msa_pool_encode(ctypes.byref(a), _lib._stream(None)) == _lib.MSA_ERR_INVALID_ARG
+    assert b"must be device memory" in lib.msa_last_error()
+    torch.cuda.synchronize()
+    assert not pageable.view(torch.int16).any()
 
 
 # ==========================================================================
