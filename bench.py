@@ -50,16 +50,17 @@ def source_digest(paths):
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(kernel):
     """HBM bytes per scan launch from the committed FETCH_SIZE / WRITE_SIZE
     counter runs (scaled by the copy calibration), or None when the record is
-    missing or was taken on a different version of the scan source."""
+    missing, covers another kernel, or was taken on a different version of
+    the scan source."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_digest(SCAN_SOURCES):
+    if rec.get("source_sha256") != source_digest(SCAN_SOURCES) or kernel not in rec.get("kernel", ""):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -77,7 +78,8 @@ def calibrate_copy():
     print(json.dumps({"calibration_copy_bytes": CALIBRATION_BYTES, "launches": 3}), flush=True)
 
 
-SCAN_KERNEL = "scan_mfma_kernel<8, 4, 1>"
+SCAN_KERNELS = {"tiled": "scan_mfma_kernel<8, 4, 1, true>", "rows": "scan_mfma_kernel<8, 4, 1, false>"}
+SCAN_KERNEL = SCAN_KERNELS["tiled"]     # the headline line's router bank is tiled
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -131,20 +133,27 @@ def write_traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     print(json.dumps(rec, indent=1))
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hip_runtime_api.h: timing-only events
+EVENT_EVERY = 4
+
+
 class HipEvents:
-    """Plain hipEvent_t pairs from the HIP runtime torch has loaded."""
+    """Plain hipEvent_t pairs from the HIP runtime torch has loaded, created
+    for timing only: without the system-scope fence a default event performs
+    when it completes (an L2 write-back and invalidate that left a ~5 us gap
+    in the stream at every record)."""
 
     def __init__(self, n):
         lib_dir = os.path.join(os.path.dirname(torch.__file__), "lib")
         self.hip = ctypes.CDLL(os.path.join(lib_dir, "libamdhip64.so"))
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.pairs = []
         for _ in range(n):
             a, b = ctypes.c_void_p(), ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
-            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(a), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(b), HIP_EVENT_DISABLE_SYSTEM_FENCE) == 0
             self.pairs.append((a, b))
 
     def elapsed_ms(self, i):
@@ -175,6 +184,8 @@ def main():
     ap.add_argument("--workload", default="bank-100M", choices=sorted(WORKLOADS),
                     help="bank-100M (default, the headline line); the others print supporting lines")
     ap.add_argument("--reps", type=int, default=10, help="timed repetitions of a supporting workload")
+    ap.add_argument("--kr-layout", default="tiled", choices=["tiled", "rows"],
+                    help="router-bank layout of the headline workload (tiled: the library's scan order)")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -205,6 +216,9 @@ def main():
     bank_tokens = int(lens.sum())
     log(f"bank: {n_docs} docs, {bank_tokens} tokens, {n_pool} pooled rows")
     kr = synth.pooled_router_bank(cfg, lens, device=dev)
+    lay = args.kr_layout
+    bank = synth.tile_router_bank(kr) if lay == "tiled" else kr      # what the scan reads
+    rkw = {"kr_layout": lay, "n_pool": n_pool}
     host_kv = synth.pooled_content_bank(cfg, lens, device=dev, pin=True)
     pool_off_d = torch.as_tensor(pool_off, device=dev)
     pool_off_h = torch.as_tensor(pool_off)
@@ -215,7 +229,8 @@ def main():
     enc_pool_off_d = torch.as_tensor(enc_pool_off, device=dev)
     enc_npool = int(enc_pool_off[-1])
     enc_kv = torch.empty((enc_npool, 2, cfg.n_kv_heads, cfg.head_dim), dtype=cfg.torch_dtype, device=dev)
-    enc_kr = torch.empty((enc_npool, cfg.n_router_heads, cfg.router_dim), dtype=cfg.torch_dtype, device=dev)
+    enc_kr = torch.empty((msa.bank_rows(enc_npool, lay), cfg.n_router_heads, cfg.router_dim), dtype=cfg.torch_dtype,
+                         device=dev)
     lk, lv = synth.local_context(cfg, device=dev)
     qrs = [synth.router_queries(cfg, step=i, device=dev) for i in range(n_steps)]
     qs = [synth.decode_queries(cfg, step=i, device=dev) for i in range(n_steps)]
@@ -239,15 +254,19 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f} s")
 
-    scan_ev = HipEvents(K)
-    dec_ev = HipEvents(K)
+    # kernel durations: event pairs attached to the scan and attention
+    # dispatches of every EVENT_EVERY-th timed step (each event point still
+    # costs the queue a ~4 us marker)
+    samples = list(range(0, K, EVENT_EVERY))
+    scan_ev = HipEvents(len(samples))
+    dec_ev = HipEvents(len(samples))
     stream = torch.cuda.current_stream()
 
     def step(i, j=None):
         msa.pool_encode(enc_bank["k"], enc_bank["v"], enc_bank["kr"], enc_bank["doc_tok_off"], enc_pool_off_d,
-                        enc.pool, enc.rope_theta, enc_npool, enc_kv, enc_kr, stream=stream)
-        msa.route(qrs[i], kr, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=asm, stream=stream,
-                  prof_events=None if j is None else scan_ev.pairs[j])
+                        enc.pool, enc.rope_theta, enc_npool, enc_kv, enc_kr, stream=stream, kr_layout=lay)
+        msa.route(qrs[i], bank, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=asm, stream=stream,
+                  prof_events=None if j is None else scan_ev.pairs[j], **rkw)
         msa.sparse_decode(qs[i], asm.mem_kv, asm.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
                           stream=stream, prof_events=None if j is None else dec_ev.pairs[j])
 
@@ -257,14 +276,14 @@ def main():
     log("warmup done")
     t0 = time.perf_counter()
     for j in range(K):
-        step(W + j, j)
+        step(W + j, j // EVENT_EVERY if j % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
     log(f"timed {K} steps: {elapsed * 1e3 / K:.3f} ms/step")
 
-    scan_ms = np.array([scan_ev.elapsed_ms(j) for j in range(K)])
-    dec_ms = np.array([dec_ev.elapsed_ms(j) for j in range(K)])
+    scan_ms = np.array([scan_ev.elapsed_ms(j) for j in range(len(samples))])
+    dec_ms = np.array([dec_ev.elapsed_ms(j) for j in range(len(samples))])
 
     # route + decode latency per step (synchronised each step), both assembly modes
     lat = {}
@@ -273,7 +292,8 @@ def main():
         for i in range(W + K, n_steps):
             torch.cuda.synchronize()
             t = time.perf_counter()
-            msa.route(qrs[i], kr, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=a, stream=stream)
+            msa.route(qrs[i], bank, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=a, stream=stream,
+                      **rkw)
             msa.sparse_decode(qs[i], a.mem_kv, a.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
                               stream=stream)
             torch.cuda.synchronize()
@@ -281,6 +301,31 @@ def main():
         lat[name] = np.array(vals)
     log(f"route+decode p50: kernel gather {np.median(lat['kernel']):.3f} ms, "
         f"copy gather {np.median(lat['copies']):.3f} ms")
+
+    # pipelined steady state: consecutive queries alternate between two
+    # streams with their own buffers (device-side assembly never waits on the
+    # host), so one query's selection, gather and decode overlap the next
+    # query's scan; the interval is the wall time per query
+    lanes = []
+    for s_ in (stream, torch.cuda.Stream()):
+        lanes.append({"s": s_, "asm": asm if s_ is stream else msa.Assembly.allocate(
+                          host_kv, pool_off_h, cfg.batch, k, mem_cap, dev, mode="kernel"),
+                      "rws": torch.empty_like(rws), "dws": torch.empty_like(dws), "dsc": torch.empty_like(doc_scores),
+                      "tki": torch.empty_like(topk_idx), "tks": torch.empty_like(topk_score),
+                      "out": torch.empty_like(out), "lse": torch.empty_like(lse)})
+    n_pipe = n_steps - (W + K)
+    for rep in range(2):                       # the first pass warms the second stream
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for n, i in enumerate(range(W + K, n_steps)):
+            L = lanes[n % 2]
+            msa.route(qrs[i], bank, pool_off_d, k, L["dsc"], L["tki"], L["tks"], L["rws"], assembly=L["asm"],
+                      stream=L["s"], **rkw)
+            msa.sparse_decode(qs[i], L["asm"].mem_kv, L["asm"].mem_len, lk, lv, loc_len, pos, cfg.rope_theta,
+                              L["out"], L["lse"], L["dws"], stream=L["s"])
+        torch.cuda.synchronize()
+        pipe_ms = (time.perf_counter() - t) * 1e3 / n_pipe
+    log(f"route+decode pipelined interval {pipe_ms:.3f} ms")
 
     scan_bytes = n_pool * cfg.n_router_heads * cfg.router_dim * 2 + cfg.n_router_heads * cfg.router_dim * 2
     scan_avg_s = scan_ms.mean() / 1e3
@@ -315,16 +360,18 @@ def main():
             "bank_tokens": bank_tokens,
             "pooled_rows": n_pool,
             "global_batch": cfg.batch,
+            "kr_layout": lay,
         },
         "roofline": {
-            "kernel": f"route bank scan ({SCAN_KERNEL})",
+            "kernel": f"route bank scan ({SCAN_KERNELS[lay]})",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic(SCAN_KERNELS[lay]),
             "scan_us": scan_ms.mean() * 1e3,
+            "timed_launches": len(samples),
             "scan_bytes": scan_bytes,
         },
         "latency_ms": {
@@ -332,6 +379,7 @@ def main():
             "route_decode_p90": float(np.percentile(lat["kernel"], 90)),
             "route_decode_p99": float(np.percentile(lat["kernel"], 99)),
             "route_decode_p50_copy_gather": float(np.percentile(lat["copies"], 50)),
+            "route_decode_pipelined_interval": float(pipe_ms),
             "roofline_floor": float(t_floor_ms),
             "decode_attention_us": float(dec_ms.mean() * 1e3),
             "decode_achieved_GBs": float(dec_bytes / (dec_ms.mean() / 1e3) / 1e9),
@@ -671,26 +719,41 @@ WORKLOADS = {"bank-100M": None, "encode-100M": workload_encode, "interleave-50M"
 def cpu_baseline(cfg, kr, pool_off, qr, seconds):
     """The float64 CPU oracle's routing on a bounded sample of the same bank:
     consecutive blocks of 2048 documents from the start of the bank, scored
-    until `seconds` of CPU time have passed."""
+    until `seconds` of CPU time have passed, on one thread (its elementwise
+    NumPy work is single-threaded anyway; BLAS is held to one thread too).
+    The first block is also timed with every thread of the process allowed."""
     import oracle
+    from threadpoolctl import threadpool_limits
 
-    cores = len(os.sched_getaffinity(0))
     qn = qr.detach().cpu().float().double().numpy()
     block = 2048
     done_docs, spent = 0, 0.0
     n_docs = len(pool_off) - 1
-    while spent < seconds and done_docs < n_docs:
-        d0, d1 = done_docs, min(done_docs + block, n_docs)
-        rows = kr[pool_off[d0]:pool_off[d1]].float().cpu().double().numpy()
-        t = time.perf_counter()
-        oracle.doc_scores(qn, rows, pool_off[d0:d1 + 1] - pool_off[d0])
-        spent += time.perf_counter() - t
-        done_docs = d1
+    with threadpool_limits(limits=1):
+        while spent < seconds and done_docs < n_docs:
+            d0, d1 = done_docs, min(done_docs + block, n_docs)
+            rows = kr[pool_off[d0]:pool_off[d1]].float().cpu().double().numpy()
+            t = time.perf_counter()
+            oracle.doc_scores(qn, rows, pool_off[d0:d1 + 1] - pool_off[d0])
+            spent += time.perf_counter() - t
+            done_docs = d1
     tokens = done_docs * 512
-    return {"value": tokens * cfg.batch / spent, "unit": "bank tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle.doc_scores (NumPy float64) over the first {done_docs} documents "
+    allowed = len(os.sched_getaffinity(0))
+    rows = kr[pool_off[0]:pool_off[block]].float().cpu().double().numpy()
+    t = time.perf_counter()
+    oracle.doc_scores(qn, rows, pool_off[:block + 1])
+    t_all = time.perf_counter() - t
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": tokens * cfg.batch / spent, "unit": "bank tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle.doc_scores (NumPy float64, one thread) over the first {done_docs} documents "
                       f"({tokens} bank tokens, {int(pool_off[done_docs])} pooled rows) of the same bank, "
-                      f"one query token, in blocks of {block} documents; {spent:.1f} s of compute"}
+                      f"one query token, in blocks of {block} documents; {spent:.1f} s of compute",
+            "all_threads_value": block * 512 * cfg.batch / t_all, "all_threads": allowed, "cpu_model": model}
 
 
 if __name__ == "__main__":

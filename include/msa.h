@@ -69,6 +69,22 @@ typedef enum {
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
 
 /* ------------------------------------------------------------------------
+ * Layouts of the pooled router-key bank Kr_bar (E = Hr * dr elements a row).
+ *
+ *  MSA_KR_ROWS (0): row-major [n_pool, Hr, dr]; the buffer holds n_pool rows.
+ *  MSA_KR_TILED (1), bf16 only: rows are grouped in tiles of 16 and a tile
+ *    stores its rows' 16-byte pieces piece-major: element e of row j is at
+ *    element offset 16*E*(j/16) + 8*(16*(e/8) + j%16) + e%8.  The buffer
+ *    holds ceil(rows/16) whole tiles (16 * E * 2 bytes each); the padding
+ *    rows of the last tile are never written by msa_pool_encode and never
+ *    reach a score in msa_route, whatever they hold.  In this order every
+ *    matrix-core operand load of the scan reads 1 KiB of contiguous memory.
+ *    The layout is a storage order of this library, not of the method: the
+ *    scores are identical, bit for bit, to those of the row-major bank.
+ * ------------------------------------------------------------------------ */
+typedef enum { MSA_KR_ROWS = 0, MSA_KR_TILED = 1 } msa_kr_layout;
+
+/* ------------------------------------------------------------------------
  * Stage 1 - offline memory encoding.
  *
  * For document d with L_d = doc_tok_off[d+1] - doc_tok_off[d] tokens and
@@ -81,7 +97,9 @@ typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
  * sources as above; "Key Technical Details" of "MSA (Memory Sparse
  * Attention) - An Open-Source Answer to AI's Memory Bottleneck").
  * Only K is rotated; V and Kr are averaged as given.  Accumulation is fp32,
- * the result is rounded to nearest-even into `dtype`.
+ * the result is rounded to nearest-even into `dtype`.  Kr_bar of pooled row
+ * j goes to bank row kr_row_base + j of kr_pooled, stored in kr_layout
+ * (MSA_KR_TILED needs bf16); kv_pooled is always row-major, row j.
  * Either output may be pinned host memory (hipHostMalloc, or torch's
  * pin_memory) instead of device memory: the kernel then writes the pooled
  * rows through the buffer's device mapping, straight over the host link -
@@ -100,7 +118,7 @@ typedef struct {
   int32_t head_dim;         /* D in {64, 128}                               */
   int32_t n_router_heads;   /* Hr >= 1                                      */
   int32_t router_dim;       /* dr in {64, 128}                              */
-  int32_t reserved0;
+  int32_t kr_layout;        /* msa_kr_layout of kr_pooled                   */
   double rope_theta;        /* > 0                                          */
   const int64_t *doc_tok_off;  /* device [n_docs+1], non-decreasing, from 0 */
   const int64_t *doc_pool_off; /* device [n_docs+1], prefix of ceil(L_d/P)  */
@@ -109,7 +127,11 @@ typedef struct {
   const void *kr;           /* device [n_tokens, Hr, dr]                    */
   void *kv_pooled;          /* out [n_pool, 2, Hkv, D]: K_bar, V_bar; device
                                or pinned host memory                        */
-  void *kr_pooled;          /* out [n_pool, Hr, dr]; device or pinned host  */
+  void *kr_pooled;          /* out: the router bank, in kr_layout; device or
+                               pinned host.  Row j of this call is written to
+                               bank row kr_row_base + j                     */
+  int64_t kr_row_base;      /* >= 0: first bank row of this call (a batch of
+                               a bank encoded in pieces)                    */
 } msa_pool_args;
 
 int msa_pool_encode(const msa_pool_args *args, void *stream);
@@ -165,10 +187,12 @@ typedef struct {
   int32_t router_dim;       /* dr in {64, 128}                              */
   int32_t top_k;            /* 1 <= k <= min(n_docs, 4096)                  */
   int32_t n_docs;
-  int32_t reserved0;
+  int32_t kr_layout;        /* msa_kr_layout of kr_pooled; TILED needs bf16
+                               and dr 64 with Hr <= 16 or dr 128 with Hr <= 8
+                               (else MSA_ERR_UNSUPPORTED)                   */
   int64_t n_pool;           /* = doc_pool_off[n_docs]                       */
   const void *qr;           /* device [B, Tq, Hr, dr]                       */
-  const void *kr_pooled;    /* device [n_pool, Hr, dr]                      */
+  const void *kr_pooled;    /* device, n_pool rows in kr_layout             */
   const int64_t *doc_pool_off; /* device [n_docs+1]; every doc >= 1 row     */
   float *doc_scores;        /* device out [B, n_docs]                       */
   int32_t *topk_idx;        /* device out [B, k]                            */
@@ -191,8 +215,9 @@ typedef struct {
   int32_t *host_mem_len;            /* pinned host in/out [B]     (copies)  */
   int32_t *host_mem_docs;           /* pinned host out [B]; opt.  (copies)  */
   void *copy_stream;                /* hipStream_t for the copies (copies)  */
-  /* profiling, optional: hipEvent_t values recorded on `stream` right before
-   * and right after the bank-scan kernel; NULL to skip */
+  /* profiling, optional: existing hipEvent_t values attached to the
+   * bank-scan kernel's dispatch (hipExtLaunchKernel): they record its start
+   * and its end, and add no packet to the queue; NULL to skip */
   void *prof_event_begin;
   void *prof_event_end;
 } msa_route_args;
@@ -247,8 +272,9 @@ typedef struct {
   float *lse;               /* device out [B, Hq]; may be NULL              */
   void *workspace;          /* device, msa_decode_workspace_bytes() bytes   */
   size_t workspace_bytes;
-  /* profiling, optional: hipEvent_t values recorded on `stream` right before
-   * and right after the split-KV attention kernel; NULL to skip */
+  /* profiling, optional: existing hipEvent_t values attached to the
+   * attention kernel's dispatch (its start and end; the split merge
+   * follows); NULL to skip */
   void *prof_event_begin;
   void *prof_event_end;
 } msa_decode_args;
@@ -306,9 +332,9 @@ typedef struct {
   float *lse;               /* device out [B, Tq, Hq]; may be NULL          */
   void *workspace;          /* device, msa_attend_workspace_bytes() bytes   */
   size_t workspace_bytes;
-  /* profiling, optional: hipEvent_t values recorded on `stream` right before
-   * and right after the attention kernel (the split merge follows); NULL to
-   * skip */
+  /* profiling, optional: existing hipEvent_t values attached to the
+   * attention kernel's dispatch (its start and end; the split merge
+   * follows); NULL to skip */
   void *prof_event_begin;
   void *prof_event_end;
 } msa_attend_args;

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     Assembly,
     MSAError,
     attend_workspace_bytes,
+    bank_rows,
     decode_workspace_bytes,
     load,
     pool_encode,
@@ -20,5 +21,5 @@ from ._lib import (  # noqa: F401
     sparse_decode,
 )
 
-__all__ = ["Assembly", "MSAError", "attend_workspace_bytes", "decode_workspace_bytes", "load", "pool_encode",
+__all__ = ["Assembly", "MSAError", "attend_workspace_bytes", "bank_rows", "decode_workspace_bytes", "load", "pool_encode",
            "route", "route_workspace_bytes", "sparse_attend", "sparse_decode", "synth"]

@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_CAPACITY, MSA_ERR_HIP = 0, -1, -2, -3, -4, -5
 MSA_F32, MSA_BF16 = 0, 1
 MSA_GATHER_COPIES, MSA_GATHER_KERNEL = 0, 1
+MSA_KR_ROWS, MSA_KR_TILED = 0, 1
+_KR_LAYOUT = {"rows": MSA_KR_ROWS, "tiled": MSA_KR_TILED}
 
 _DTYPE = {torch.float32: MSA_F32, torch.bfloat16: MSA_BF16}
 
@@ -35,16 +37,16 @@ class PoolArgs(ctypes.Structure):
     _fields_ = [
         ("dtype", I32), ("n_docs", I32), ("n_tokens", I64), ("n_pool", I64),
         ("pool_size", I32), ("n_kv_heads", I32), ("head_dim", I32), ("n_router_heads", I32),
-        ("router_dim", I32), ("reserved0", I32), ("rope_theta", ctypes.c_double),
+        ("router_dim", I32), ("kr_layout", I32), ("rope_theta", ctypes.c_double),
         ("doc_tok_off", P), ("doc_pool_off", P), ("k", P), ("v", P), ("kr", P),
-        ("kv_pooled", P), ("kr_pooled", P),
+        ("kv_pooled", P), ("kr_pooled", P), ("kr_row_base", I64),
     ]
 
 
 class RouteArgs(ctypes.Structure):
     _fields_ = [
         ("dtype", I32), ("batch", I32), ("q_tokens", I32), ("n_router_heads", I32),
-        ("router_dim", I32), ("top_k", I32), ("n_docs", I32), ("reserved0", I32), ("n_pool", I64),
+        ("router_dim", I32), ("top_k", I32), ("n_docs", I32), ("kr_layout", I32), ("n_pool", I64),
         ("qr", P), ("kr_pooled", P), ("doc_pool_off", P), ("doc_scores", P), ("topk_idx", P),
         ("topk_score", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
         ("host_kv", P), ("host_doc_pool_off", P), ("kv_dtype", I32), ("n_kv_heads", I32), ("head_dim", I32),
@@ -167,24 +169,48 @@ def dtype_code(dtype):
 # stage 1
 # --------------------------------------------------------------------------
 
+def _layout_code(kr_layout):
+    try:
+        return _KR_LAYOUT[kr_layout]
+    except KeyError:
+        raise ValueError(f"kr_layout must be 'rows' or 'tiled', got {kr_layout!r}") from None
+
+
+def bank_rows(n_rows, kr_layout="rows"):
+    """Rows a router-bank buffer holds for n_rows rows: the tiled layout
+    stores whole 16-row tiles."""
+    return -(-n_rows // 16) * 16 if _layout_code(kr_layout) == MSA_KR_TILED else n_rows
+
+
 def pool_encode(k, v, kr, doc_tok_off, doc_pool_off, pool_size, rope_theta, n_pool,
-                kv_pooled=None, kr_pooled=None, stream=None):
+                kv_pooled=None, kr_pooled=None, stream=None, kr_layout="rows", kr_row_base=0):
     """msa_pool_encode.  k, v: [T, Hkv, D]; kr: [T, Hr, dr] (device, same
     dtype); offsets: int64 device [n_docs+1].  The outputs may be device
     tensors or pinned CPU tensors (written straight over the host link).
-    Returns (kv_pooled, kr_pooled)."""
+    kr_pooled is the router bank in `kr_layout` ("rows" or "tiled"); this
+    call writes its rows kr_row_base .. kr_row_base + n_pool.  Returns
+    (kv_pooled, kr_pooled)."""
     n_tok, hkv, d = k.shape
     _, hr, dr = kr.shape
+    lay = _layout_code(kr_layout)
     if kv_pooled is None:
         kv_pooled = torch.empty((n_pool, 2, hkv, d), dtype=k.dtype, device=k.device)
     if kr_pooled is None:
-        kr_pooled = torch.empty((n_pool, hr, dr), dtype=k.dtype, device=k.device)
+        kr_pooled = torch.empty((bank_rows(kr_row_base + n_pool, kr_layout), hr, dr), dtype=k.dtype,
+                                device=k.device)
+    if kv_pooled.numel() < n_pool * 2 * hkv * d:
+        raise ValueError(f"kv_pooled holds {kv_pooled.numel()} elements, {n_pool} rows need {n_pool * 2 * hkv * d}")
+    need = bank_rows(kr_row_base + n_pool, kr_layout) * hr * dr
+    if kr_pooled.numel() < need:
+        raise ValueError(f"kr_pooled holds {kr_pooled.numel()} elements, rows up to {kr_row_base + n_pool} in the "
+                         f"{kr_layout} layout need {need}")
     a = PoolArgs(dtype=dtype_code(k.dtype), n_docs=doc_tok_off.numel() - 1, n_tokens=n_tok, n_pool=n_pool,
                  pool_size=pool_size, n_kv_heads=hkv, head_dim=d, n_router_heads=hr, router_dim=dr,
                  rope_theta=float(rope_theta), doc_tok_off=_dptr(doc_tok_off, "doc_tok_off"),
                  doc_pool_off=_dptr(doc_pool_off, "doc_pool_off"), k=_dptr(k, "k"), v=_dptr(v, "v"),
                  kr=_dptr(kr, "kr"), kv_pooled=_dptr(kv_pooled, "kv_pooled", pinned_ok=True),
-                 kr_pooled=_dptr(kr_pooled, "kr_pooled", pinned_ok=True))
+                 kr_pooled=_dptr(kr_pooled, "kr_pooled", pinned_ok=True), kr_layout=lay,
+                 kr_row_base=kr_row_base)
     _check(load().msa_pool_encode(ctypes.byref(a), _stream(stream)))
     return kv_pooled, kr_pooled
 
@@ -230,12 +256,20 @@ class Assembly:
 
 
 def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, topk_score=None,
-          workspace=None, assembly=None, stream=None, prof_events=None):
-    """msa_route.  qr: [B, Tq, Hr, dr]; kr_pooled: [n_pool, Hr, dr];
-    doc_pool_off: int64 device [n_docs+1].  Returns (topk_idx, topk_score,
-    doc_scores)."""
+          workspace=None, assembly=None, stream=None, prof_events=None, kr_layout="rows", n_pool=None):
+    """msa_route.  qr: [B, Tq, Hr, dr]; kr_pooled: the router bank in
+    `kr_layout` ("rows": [n_pool, Hr, dr]; "tiled": whole 16-row tiles,
+    n_pool given); doc_pool_off: int64 device [n_docs+1].  Returns
+    (topk_idx, topk_score, doc_scores)."""
     b, tq, hr, dr = qr.shape
-    n_pool = kr_pooled.shape[0]
+    lay = _layout_code(kr_layout)
+    if n_pool is None:
+        if lay == MSA_KR_TILED:
+            raise ValueError("n_pool is required with the tiled layout")
+        n_pool = kr_pooled.shape[0]
+    if kr_pooled.numel() < bank_rows(n_pool, kr_layout) * hr * dr:
+        raise ValueError(f"kr_pooled holds {kr_pooled.numel()} elements, {n_pool} rows in the {kr_layout} layout "
+                         f"need {bank_rows(n_pool, kr_layout) * hr * dr}")
     n_docs = doc_pool_off.numel() - 1
     dev = qr.device
     if doc_scores is None:
@@ -251,7 +285,7 @@ def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, to
                   top_k=top_k, n_docs=n_docs, n_pool=n_pool, qr=_dptr(qr, "qr"), kr_pooled=_dptr(kr_pooled, "kr_pooled"),
                   doc_pool_off=_dptr(doc_pool_off, "doc_pool_off"), doc_scores=_dptr(doc_scores, "doc_scores"),
                   topk_idx=_dptr(topk_idx, "topk_idx"), topk_score=_dptr(topk_score, "topk_score"),
-                  workspace=_dptr(workspace, "workspace"), workspace_bytes=workspace.numel())
+                  workspace=_dptr(workspace, "workspace"), workspace_bytes=workspace.numel(), kr_layout=lay)
     if assembly is not None:
         asm = assembly
         a.host_kv = _hptr(asm.host_kv, "host_kv", pinned=asm.mode == "kernel")

@@ -491,18 +491,15 @@ static hipError_t launch_attend_t(const msa_attend_args &a, float *part_acc, flo
   const int64_t items = (int64_t)a.batch * a.n_kv_heads * p.n_mt * p.n_split;
   const int64_t grid = (items + kAWaves - 1) / kAWaves;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a.prof_event_begin);
-  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a.prof_event_end);
   hipError_t e = hipSuccess;
-  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((attend_kernel<D>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
-                     reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
-                     a.mem_len, reinterpret_cast<const uint16_t *>(a.local_k),
-                     reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset, part_acc, part_ml,
-                     a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap, a.local_cap, p.n_mt, p.n_split,
-                     p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
+  hipExtLaunchKernelGGL((attend_kernel<D>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
+                        prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
+                        reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
+                        a.mem_len, reinterpret_cast<const uint16_t *>(a.local_k),
+                        reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset, part_acc,
+                        part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap, a.local_cap, p.n_mt,
+                        p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
   const int64_t rows = (int64_t)a.batch * a.q_tokens * a.n_q_heads;
   hipLaunchKernelGGL((attend_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, s, part_acc, part_ml,
                      reinterpret_cast<uint16_t *>(a.out), a.lse, a.q_tokens, a.n_q_heads, a.n_kv_heads, p.n_mt,

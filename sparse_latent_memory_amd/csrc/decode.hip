@@ -329,18 +329,15 @@ template <typename T, int D>
 hipError_t launch_t(const msa_decode_args &a, float *part_acc, float *part_ml, int32_t n_split, hipStream_t s) {
   const int split_len = choose_split_len(a.batch, a.mem_cap, a.local_cap);
   const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.0f / sqrtf((float)a.head_dim);
-  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a.prof_event_begin);
-  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a.prof_event_end);
   hipError_t e = hipSuccess;
   if (n_split > kMaxSplit) return hipErrorInvalidValue;
-  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(n_split, a.n_kv_heads, a.batch), dim3(256), 0, s,
-                     reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.mem_kv), a.mem_len,
-                     reinterpret_cast<const T *>(a.local_k), reinterpret_cast<const T *>(a.local_v),
-                     a.local_len, a.pos_offset, part_acc, part_ml, a.n_q_heads, a.n_kv_heads, a.mem_cap,
-                     a.local_cap, split_len, n_split, scale * kLog2e, log2(a.rope_theta));
+  hipExtLaunchKernelGGL((decode_split_kernel<T, D>), dim3(n_split, a.n_kv_heads, a.batch), dim3(256), 0, s,
+                        prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
+                        reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.mem_kv), a.mem_len,
+                        reinterpret_cast<const T *>(a.local_k), reinterpret_cast<const T *>(a.local_v),
+                        a.local_len, a.pos_offset, part_acc, part_ml, a.n_q_heads, a.n_kv_heads, a.mem_cap,
+                        a.local_cap, split_len, n_split, scale * kLog2e, log2(a.rope_theta));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.batch * a.n_q_heads), dim3(256), 0, s, part_acc,
                      part_ml, reinterpret_cast<T *>(a.out), a.lse, n_split);
   return hipGetLastError();

@@ -100,6 +100,12 @@ int msa_pool_encode(const msa_pool_args *a, void *stream) {
                 (long long)a->n_pool, (long long)a->n_tokens);
   if (!dim_ok(a->head_dim) || !dim_ok(a->router_dim))
     return fail(MSA_ERR_UNSUPPORTED, "msa_pool_encode: head_dim and router_dim must be 64 or 128");
+  if (a->kr_layout != MSA_KR_ROWS && a->kr_layout != MSA_KR_TILED)
+    return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: bad kr_layout %d", a->kr_layout);
+  if (a->kr_layout == MSA_KR_TILED && a->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "msa_pool_encode: the tiled router-bank layout is bf16 only");
+  if (a->kr_row_base < 0)
+    return fail(MSA_ERR_INVALID_ARG, "msa_pool_encode: kr_row_base must be >= 0");
   const int vw = a->dtype == MSA_BF16 ? 8 : 4;
   const int tasks = a->n_kv_heads * a->head_dim / 2 / vw + a->n_kv_heads * a->head_dim / vw +
                     a->n_router_heads * a->router_dim / vw;
@@ -166,6 +172,11 @@ int msa_route(const msa_route_args *a, void *stream) {
     return fail(MSA_ERR_UNSUPPORTED,
                 "msa_route: router_dim must be 64 or 128 and n_router_heads a power of two dividing 64 with "
                 "n_router_heads * router_dim <= 2048");
+  if (a->kr_layout != MSA_KR_ROWS && a->kr_layout != MSA_KR_TILED)
+    return fail(MSA_ERR_INVALID_ARG, "msa_route: bad kr_layout %d", a->kr_layout);
+  if (a->kr_layout == MSA_KR_TILED && (a->dtype != MSA_BF16 || !mfma_shape(a->n_router_heads, a->router_dim)))
+    return fail(MSA_ERR_UNSUPPORTED, "msa_route: the tiled router-bank layout needs bf16 and a matrix-core "
+                                     "router shape (dr 64 with Hr <= 16, or dr 128 with Hr <= 8)");
   if (!a->qr || !a->kr_pooled || !a->doc_pool_off || !a->doc_scores || !a->topk_idx || !a->topk_score)
     return fail(MSA_ERR_INVALID_ARG, "msa_route: NULL pointer");
   if (!aligned16(a->qr) || !aligned16(a->kr_pooled))

@@ -1,6 +1,7 @@
 // Internal declarations shared by the libmsa translation units (gfx950 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,6 +9,11 @@
 #include "msa_device.h"
 
 namespace msa {
+
+// Optional profiling events of a call, attached to one kernel's dispatch
+// (hipExtLaunchKernel): they time exactly that kernel and add no packets to
+// the queue, unlike event records placed around the launch.
+inline hipEvent_t prof_event(void *p) { return reinterpret_cast<hipEvent_t>(p); }
 
 // ---------------------------------------------------------------------------
 // launchers (validated arguments only)

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(512) void pool_kernel(
     const T *__restrict__ k, const T *__restrict__ v, const T *__restrict__ kr,
     const int64_t *__restrict__ tok_off, const int64_t *__restrict__ pool_off,
     T *__restrict__ kv_out, T *__restrict__ kr_out, int n_docs, int64_t n_tokens, int64_t n_pool,
-    int P, int Hkv, int D, int Hr, int dr, double log2_theta) {
+    int P, int Hkv, int D, int Hr, int dr, double log2_theta, int kr_tiled, int64_t kr_row_base) {
   constexpr int VW = Elt<T>::kPerVec;
   __shared__ double omega[64];
   const int half = D / 2;
@@ -56,7 +56,6 @@ __global__ __launch_bounds__(512) void pool_kernel(
 
   for (int slot = threadIdx.x; slot < n_slots; slot += blockDim.x) {
     const bool is_k = slot < n_kp * KSPL;
-    const int spl = is_k ? KSPL : VSPL;
     const int task = is_k ? slot / KSPL : (slot - n_kp * KSPL) / VSPL;
     const int part = is_k ? slot % KSPL : (slot - n_kp * KSPL) % VSPL;
     int e = 0, h = 0, j0 = 0;
@@ -178,7 +177,12 @@ __global__ __launch_bounds__(512) void pool_kernel(
         if (part == 0) {
 #pragma unroll
           for (int i = 0; i < VW; ++i) acc[i] *= inv_n;
-          T *out = is_v ? kv_out + row * 2 * krow + krow + e : kr_out + row * rrow + e;
+          // Kr goes to bank row R; in the tiled bank a 16-row tile stores its
+          // rows' VW-element pieces piece-major
+          const int64_t R = kr_row_base + row;
+          T *out = is_v       ? kv_out + row * 2 * krow + krow + e
+                   : kr_tiled ? kr_out + (R >> 4) * 16 * rrow + (16 * (e / VW) + (R & 15)) * VW
+                              : kr_out + R * rrow + e;
           st16(out, Elt<T>::pack(acc));
         }
       }
@@ -206,7 +210,7 @@ hipError_t launch_pool_t(const msa_pool_args &a, hipStream_t s) {
                      reinterpret_cast<const T *>(a.kr), a.doc_tok_off, a.doc_pool_off,
                      reinterpret_cast<T *>(a.kv_pooled), reinterpret_cast<T *>(a.kr_pooled), a.n_docs,
                      a.n_tokens, a.n_pool, a.pool_size, a.n_kv_heads, a.head_dim, a.n_router_heads,
-                     a.router_dim, log2(a.rope_theta));
+                     a.router_dim, log2(a.rope_theta), a.kr_layout == MSA_KR_TILED ? 1 : 0, a.kr_row_base);
   return hipGetLastError();
 }
 

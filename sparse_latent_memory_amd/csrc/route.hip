@@ -78,25 +78,20 @@ size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t h
 
 hipError_t launch_route(const msa_route_args &a, const RouteWs &ws, const void *host_kv_dev, hipStream_t s) {
   const int M = a.batch * a.q_tokens;
-  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(a.prof_event_begin);
-  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(a.prof_event_end);
   hipError_t e = hipSuccess;
+  // the scan launchers attach a.prof_event_begin / _end to the scan kernel
   if (narrow_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
-    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
     e = launch_scan_narrow(a, ws.row_score, s);
   } else {
     if ((e = launch_prep_unit(a, ws.qhat, s)) != hipSuccess) return e;
     if (wide_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
       if ((e = launch_prep_wide(a, ws.qhat, ws.wide_frag, s)) != hipSuccess) return e;
-      if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
       e = launch_scan_wide(a, ws.wide_frag, ws.row_score, s);
     } else {
-      if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
       e = launch_scan_valu(a, ws.qhat, ws.row_score, s);
     }
   }
   if (e != hipSuccess) return e;
-  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
   return launch_select(a, ws, host_kv_dev, s);
 }
 

@@ -29,9 +29,14 @@ constexpr int kWaves = 4;   // waves per workgroup
 // A-fragment f = h*KS + s, lane l holds A[row = l%16][k = 32 s + 8 (l/16) + e]
 // (e < 8) of head h.  Row 2m is the bf16 rounding of unit query token m, row
 // 2m+1 the bf16 rounding of its remainder; rows of absent tokens are zero.
-// Lane l owns bank row (tile*16 + l%16) and the same k slice, so one load
-// instruction of the wave reads 16 rows x 64 contiguous bytes.  Heads are
-// loaded in groups of HG, one group ahead of the MFMAs that consume them.
+// Lane l owns bank row (tile*16 + l%16) and the same k slice.  In the
+// row-major bank one load instruction of the wave reads 16 rows x 64
+// contiguous bytes; in the tiled bank (16-byte pieces of a 16-row tile
+// stored piece-major) fragment f of the tile is the contiguous 1 KiB at
+// 1024 f, lane l's 16 bytes at 16 l, and the loads are non-temporal: a
+// streaming read of that order runs ~10% faster than of the row order.
+// Heads are loaded in groups of HG, one group ahead of the MFMAs that
+// consume them.
 #ifndef MSA_SCAN_HG
 #define MSA_SCAN_HG 1
 #endif
@@ -47,13 +52,22 @@ constexpr int kWaves = 4;   // waves per workgroup
 #ifndef MSA_SCAN_GRID_MULT // workgroups launched per resident workgroup slot
 #define MSA_SCAN_GRID_MULT 1
 #endif
+#ifndef MSA_SCAN_TILED_NT  // 1: non-temporal loads from the tiled bank
+#define MSA_SCAN_TILED_NT 1
+#endif
 #if MSA_SCAN_NT
 #define SCAN_LD ld16_nt
 #else
 #define SCAN_LD ld16
 #endif
 
-template <int HR, int KS, int HG>
+template <bool TILED>
+__device__ __forceinline__ u32x4 scan_ld(const uint16_t *p) {
+  if constexpr (TILED && MSA_SCAN_TILED_NT) return ld16_nt(p);
+  else return SCAN_LD(p);
+}
+
+template <int HR, int KS, int HG, bool TILED>
 __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restrict__ kr,
                                                         const uint16_t *__restrict__ qr,
                                                         float *__restrict__ row_score, int64_t n_pool, int B,
@@ -115,11 +129,19 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
        tile += (int64_t)gridDim.x * kWaves) {
 #endif
     const int64_t row = tile * 16 + col;
-    const int64_t rowc = row < n_pool ? row : n_pool - 1;
-    const uint16_t *rp = kr + rowc * ROW + 8 * grp;
+    // fragment f of this lane at rp + FS * f (the tiled bank holds whole
+    // tiles; the row-major one is clamped to its last row)
+    constexpr int FS = TILED ? 512 : 32;
+    const uint16_t *rp;
+    if constexpr (TILED) {
+      rp = kr + tile * (16 * ROW) + 8 * lane;
+    } else {
+      const int64_t rowc = row < n_pool ? row : n_pool - 1;
+      rp = kr + rowc * ROW + 8 * grp;
+    }
     u32x4 cur[GF];
 #pragma unroll
-    for (int f = 0; f < GF; ++f) cur[f] = SCAN_LD(rp + 32 * f);
+    for (int f = 0; f < GF; ++f) cur[f] = scan_ld<TILED>(rp + FS * f);
 
     float sc0 = 0.f, sc1 = 0.f;
 #if MSA_SCAN_PIPE
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
       u32x4 nxt[GF];
       if (gi + 1 < NG) {
 #pragma unroll
-        for (int f = 0; f < GF; ++f) nxt[f] = SCAN_LD(rp + 32 * ((gi + 1) * GF + f));
+        for (int f = 0; f < GF; ++f) nxt[f] = scan_ld<TILED>(rp + FS * ((gi + 1) * GF + f));
       }
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
@@ -180,21 +202,29 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
   }
 }
 
-template <int HR, int KS>
-hipError_t launch_scan_mfma(const msa_route_args &a, float *row_score, hipStream_t s) {
+template <int HR, int KS, bool TILED>
+hipError_t launch_scan_mfma_t(const msa_route_args &a, float *row_score, hipStream_t s) {
   constexpr int HG = HR < MSA_SCAN_HG ? HR : MSA_SCAN_HG;
   const int64_t n_tiles = (a.n_pool + 15) / 16;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_mfma_kernel<HR, KS, HG>, 256, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_mfma_kernel<HR, KS, HG, TILED>, 256, 0) !=
+          hipSuccess ||
       occ < 1)
     occ = 1;
   const int64_t want = (int64_t)device_info().n_cu * occ * MSA_SCAN_GRID_MULT;
   const int64_t need = (n_tiles + kWaves - 1) / kWaves;
   const int grid = (int)std::max<int64_t>(1, std::min(want, need));
-  hipLaunchKernelGGL((scan_mfma_kernel<HR, KS, HG>), dim3(grid), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t *>(a.kr_pooled), reinterpret_cast<const uint16_t *>(a.qr),
-                     row_score, a.n_pool, a.batch, a.q_tokens);
+  hipExtLaunchKernelGGL((scan_mfma_kernel<HR, KS, HG, TILED>), dim3(grid), dim3(256), 0, s,
+                        prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
+                        reinterpret_cast<const uint16_t *>(a.kr_pooled), reinterpret_cast<const uint16_t *>(a.qr),
+                        row_score, a.n_pool, a.batch, a.q_tokens);
   return hipGetLastError();
+}
+
+template <int HR, int KS>
+hipError_t launch_scan_mfma(const msa_route_args &a, float *row_score, hipStream_t s) {
+  return a.kr_layout == MSA_KR_TILED ? launch_scan_mfma_t<HR, KS, true>(a, row_score, s)
+                                     : launch_scan_mfma_t<HR, KS, false>(a, row_score, s);
 }
 
 }  // namespace

@@ -217,6 +217,27 @@ def pooled_router_bank(cfg, lens, device="cpu"):
     return _pooled_rows(cfg, T_KR, lens, (cfg.n_router_heads, cfg.router_dim), device)
 
 
+def tile_router_bank(kr, pad_value=0.0):
+    """A row-major router bank [n, Hr, dr] re-laid out in the library's tiled
+    order: whole 16-row tiles, each storing its rows' 16-byte pieces
+    piece-major.  A permutation of the elements (padding rows = pad_value);
+    returned as [ceil(n/16)*16, Hr, dr] so that it indexes like the rows."""
+    n, hr, dr = kr.shape
+    pe = 16 // kr.element_size()
+    nt = -(-n // 16)
+    rows = torch.full((nt * 16, hr, dr), pad_value, dtype=kr.dtype, device=kr.device)
+    rows[:n] = kr
+    return rows.view(nt, 16, hr * dr // pe, pe).permute(0, 2, 1, 3).contiguous().view(nt * 16, hr, dr)
+
+
+def untile_router_bank(kt, n):
+    """Inverse of tile_router_bank: the first n rows, row-major."""
+    rows16, hr, dr = kt.shape
+    pe = 16 // kt.element_size()
+    nt = rows16 // 16
+    return kt.view(nt, hr * dr // pe, 16, pe).permute(0, 2, 1, 3).contiguous().view(rows16, hr, dr)[:n]
+
+
 def pooled_content_bank(cfg, lens, device="cpu", pin=False):
     """K_bar/V_bar [n_pool, 2, Hkv, D] drawn in pooled space.  With pin=True
     the result lives in pinned host memory (drawn on `device` block by block)."""

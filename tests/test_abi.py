@@ -114,11 +114,46 @@ def _call_pool(a):
     ("n_pool", 1000, _lib.MSA_ERR_INVALID_ARG),
     ("k", None, _lib.MSA_ERR_INVALID_ARG),
     ("kv_pooled", ctypes.c_void_p(_B + 8), _lib.MSA_ERR_INVALID_ARG),   # misaligned
+    ("kr_layout", 2, _lib.MSA_ERR_INVALID_ARG),
+    ("kr_row_base", -1, _lib.MSA_ERR_INVALID_ARG),
 ])
 def test_pool_rejects_bad_arguments(field, value, code):
     status, msg = _call_pool(_pool_args(**{field: value}))
     assert status == code, msg
     assert msg.startswith("msa_pool_encode")
+
+
+@no_gpu
+def test_tiled_router_bank_needs_bf16_and_a_matrix_core_shape():
+    status, msg = _call_pool(_pool_args(dtype=0, kr_layout=_lib.MSA_KR_TILED))
+    assert status == _lib.MSA_ERR_UNSUPPORTED and "bf16" in msg
+    lib = _lib.load()
+    for kw in ({"dtype": 0}, {"n_router_heads": 16, "router_dim": 128}, {"n_router_heads": 32, "router_dim": 64}):
+        a = _route_args(kr_layout=_lib.MSA_KR_TILED, **kw)
+        assert lib.msa_route(ctypes.byref(a), None) == _lib.MSA_ERR_UNSUPPORTED, lib.msa_last_error()
+        assert b"tiled" in lib.msa_last_error()
+    a = _route_args(kr_layout=2)
+    assert lib.msa_route(ctypes.byref(a), None) == _lib.MSA_ERR_INVALID_ARG
+
+
+@no_gpu
+def test_binding_checks_router_bank_sizes():
+    """An undersized bank buffer is refused by the binding before any call
+    (the library cannot see a raw pointer's extent)."""
+    import sparse_latent_memory_amd as msa
+    bf = torch.bfloat16
+    qr = torch.zeros(1, 1, 8, 128, dtype=bf)
+    off = torch.tensor([0, 20], dtype=torch.int64)
+    with pytest.raises(ValueError, match="n_pool is required"):
+        msa.route(qr, torch.zeros(32, 8, 128, dtype=bf), off, 1, kr_layout="tiled")
+    with pytest.raises(ValueError, match="need"):
+        msa.route(qr, torch.zeros(20, 8, 128, dtype=bf), off, 1, kr_layout="tiled", n_pool=20)
+    with pytest.raises(ValueError, match="kr_layout must be"):
+        msa.route(qr, torch.zeros(20, 8, 128, dtype=bf), off, 1, kr_layout="cols")
+    k = torch.zeros(100, 8, 128, dtype=bf)
+    with pytest.raises(ValueError, match="kr_pooled holds"):
+        msa.pool_encode(k, k, k, off, off, 64, 1e6, 2, kr_pooled=torch.zeros(16, 8, 128, dtype=bf),
+                        kr_layout="tiled", kr_row_base=15)
 
 
 @no_gpu
@@ -275,3 +310,28 @@ def test_binding_refuses_host_tensors_for_device_arguments():
     with pytest.raises(ValueError, match="pinned CPU tensor"):
         _lib._hptr(torch.zeros(4), "host_kv", pinned=True)
     assert _lib._hptr(torch.zeros(4), "host_doc_pool_off") is not None
+
+
+def test_tiled_bank_helpers_follow_the_declared_layout():
+    """synth.tile_router_bank puts element e of row j at
+    16*E*(j/16) + 8*(16*(e/8) + j%16) + e%8, as msa.h declares for
+    MSA_KR_TILED, and untile_router_bank inverts it."""
+    from sparse_latent_memory_amd import synth
+    for n, hr, dr in [(37, 2, 64), (16, 8, 128), (1, 1, 64)]:
+        e_row = hr * dr
+        ids = (torch.arange(n * e_row, dtype=torch.int32) % 30011).to(torch.int16)
+        bank = ids.view(n, hr, dr).view(torch.bfloat16)
+        flat = synth.tile_router_bank(bank, pad_value=-1.0).view(torch.int16).view(-1)
+        assert flat.numel() == -(-n // 16) * 16 * e_row
+        j = torch.arange(n).view(n, 1)
+        e = torch.arange(e_row).view(1, e_row)
+        off = 16 * e_row * (j // 16) + 8 * (16 * (e // 8) + j % 16) + e % 8
+        assert torch.equal(flat[off.reshape(-1)], ids)
+        back = synth.untile_router_bank(synth.tile_router_bank(bank), n)
+        assert torch.equal(back.view(torch.int16), bank.view(torch.int16))
+    assert msa_bank_rows(37) == (37, 48)
+
+
+def msa_bank_rows(n):
+    import sparse_latent_memory_amd as msa
+    return msa.bank_rows(n, "rows"), msa.bank_rows(n, "tiled")

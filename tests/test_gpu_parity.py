@@ -158,6 +158,46 @@ def test_pool_into_pinned_host_tier():
     assert not pageable.view(torch.int16).any()
 
 
+def test_pool_tiled_router_bank_at_row_offsets():
+    """Kr_bar written into a tiled bank at an unaligned first row equals the
+    row-major output bit for bit, rows outside the call untouched; the bank
+    encoded in two batches (each at its own first row) equals the one-call
+    bank."""
+    cfg = synth.config(2, n_docs=96)
+    bank = synth.raw_bank(cfg, device=DEV)
+    lens = bank["lens"]
+    off_h = synth.row_offsets(lens, cfg.pool)
+    n_pool = int(off_h[-1])
+    _say(f"pool: tiled router bank, {len(lens)} docs, {n_pool} rows at row 5")
+    kv_r, kr_r = msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], _dev(off_h), cfg.pool,
+                                 cfg.rope_theta, n_pool)
+    base = 5
+    sentinel = torch.full((msa.bank_rows(base + n_pool, "tiled"), 8, 128), -3.0, dtype=torch.bfloat16, device=DEV)
+    kt = sentinel.clone()
+    kv_t, _ = msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], _dev(off_h), cfg.pool,
+                              cfg.rope_theta, n_pool, kr_pooled=kt, kr_layout="tiled", kr_row_base=base)
+    torch.cuda.synchronize()
+    rows = synth.untile_router_bank(kt, kt.shape[0])
+    assert torch.equal(rows[base:base + n_pool].view(torch.int16), kr_r.view(torch.int16))
+    assert torch.equal(rows[:base].view(torch.int16), sentinel[:base].view(torch.int16))
+    assert torch.equal(rows[base + n_pool:].view(torch.int16), sentinel[base + n_pool:].view(torch.int16))
+    assert torch.equal(kv_t.view(torch.int16), kv_r.view(torch.int16))
+    # two batches: documents [0, 37) and [37, 96), the second at the first's end
+    whole = synth.tile_router_bank(kr_r, pad_value=-3.0)
+    kt2 = torch.full_like(whole, -3.0)
+    tok = synth.token_offsets(lens)
+    d1 = 37
+    for d0, d_end in [(0, d1), (d1, len(lens))]:
+        t0, t1 = int(tok[d0]), int(tok[d_end])
+        toff = _dev(tok[d0:d_end + 1] - tok[d0])
+        poff = off_h[d0:d_end + 1] - off_h[d0]
+        msa.pool_encode(bank["k"][t0:t1], bank["v"][t0:t1], bank["kr"][t0:t1], toff, _dev(poff), cfg.pool,
+                        cfg.rope_theta, int(poff[-1]), kr_pooled=kt2, kr_layout="tiled", kr_row_base=int(off_h[d0]))
+    torch.cuda.synchronize()
+    assert int(off_h[d1]) % 16 != 0
+    assert torch.equal(kt2.view(torch.int16), whole.view(torch.int16))
+
+
 # ==========================================================================
 # stage 2: routing
 # ==========================================================================
@@ -353,6 +393,79 @@ def test_route_100m_bank_sampled():
     # every selected document beats every sampled unselected one, up to tau
     assert ref[sel].min() >= ref[~sel].max() - TAU
     check_topk_order(idx[None], np64(sc))
+
+
+def _route_both_layouts(qr, kr, off, k, what, pad_value=float("nan")):
+    """Route the row-major bank and its tiled copy (padding rows hold
+    pad_value): every output must be identical, bit for bit."""
+    n_pool = int(off[-1])
+    kt = synth.tile_router_bank(kr, pad_value=pad_value)
+    assert kt.shape[0] == msa.bank_rows(n_pool, "tiled")
+    idx_r, sc_r, dsc_r = msa.route(qr, kr, _dev(off), k)
+    idx_t, sc_t, dsc_t = msa.route(qr, kt, _dev(off), k, kr_layout="tiled", n_pool=n_pool)
+    torch.cuda.synchronize()
+    assert torch.equal(dsc_t.view(torch.int32), dsc_r.view(torch.int32)), f"{what}: doc scores differ"
+    assert torch.equal(idx_t, idx_r), f"{what}: top-k differs"
+    assert torch.equal(sc_t.view(torch.int32), sc_r.view(torch.int32)), f"{what}: top-k scores differ"
+    return idx_t, dsc_t
+
+
+@pytest.mark.parametrize("hr,dr", [(8, 128), (4, 64), (1, 128), (16, 64), (2, 64)])
+@pytest.mark.parametrize("b,tq", [(1, 1), (3, 2), (8, 1), (16, 1), (2, 100)])
+def test_route_tiled_bank_matches_row_major(hr, dr, b, tq):
+    """The tiled router bank gives the row-major bank's results bit for bit
+    (narrow and wide scans), with NaN in the padding rows of its last tile;
+    one case is also checked against the oracle."""
+    g = torch.Generator().manual_seed(900 + hr * dr + b * 7 + tq)
+    kr, off = _ragged_bank(g, 301, 17, hr, dr, torch.bfloat16)
+    qr = _randn(g, b, tq, hr, dr, dtype=torch.bfloat16).to(DEV)
+    _say(f"route: tiled bank, Hr={hr} dr={dr} B={b} Tq={tq}, {int(off[-1])} rows")
+    idx, dsc = _route_both_layouts(qr, kr, off, 16, f"tiled Hr={hr} dr={dr} B={b} Tq={tq}")
+    if hr == 8 and b * tq in (1, 200):
+        ref = oracle.doc_scores(np64(qr), np64(kr), off)
+        check_scores(np64(dsc), ref, "tiled vs oracle")
+        check_topk(np64(idx), ref, 16, "tiled vs oracle")
+
+
+@pytest.mark.parametrize("b,tq", [(1, 256), (1, 1)])
+def test_route_tiled_bank_ragged_tail_sizes(b, tq):
+    """Banks of 1..33 rows (a partial last tile of every size) and a bank
+    whose last tile is whole."""
+    g = torch.Generator().manual_seed(77 + tq)
+    for n_rows in [1, 2, 15, 16, 17, 31, 33]:
+        rows = np.ones(n_rows, dtype=np.int64)
+        off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+        kr = _randn(g, n_rows, 8, 128, dtype=torch.bfloat16).to(DEV)
+        qr = _randn(g, b, tq, 8, 128, dtype=torch.bfloat16).to(DEV)
+        _route_both_layouts(qr, kr, off, min(4, n_rows), f"{n_rows} rows, B={b} Tq={tq}")
+
+
+def test_route_tiled_needle_bank_full_size():
+    """The 16.8M-token needle bank (275K rows) tiled: identical to the
+    row-major results, and every needle is selected."""
+    cfg = synth.config(3)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    kr = synth.pooled_router_bank(cfg, lens, device=DEV)
+    qr = synth.router_queries(cfg, device=DEV)
+    needles = synth.plant_needles(cfg, qr, kr, off)
+    _say(f"route: tiled needle bank, {off[-1]} rows, B={cfg.batch}")
+    idx, _ = _route_both_layouts(qr, kr, off, cfg.top_k, "tiled needle bank")
+    idx = np64(idx)
+    assert all(needles[b] in idx[b] for b in range(cfg.batch))
+
+
+@pytest.mark.slow
+def test_route_100m_bank_tiled_matches_row_major():
+    """The 100M-token bank (1,562,504 rows) in the tiled layout: one query
+    token, results identical to the row-major bank's."""
+    cfg = synth.config(4)
+    lens = synth.doc_lengths(cfg)
+    off = synth.row_offsets(lens, cfg.pool)
+    kr = synth.pooled_router_bank(cfg, lens, device=DEV)
+    qr = synth.router_queries(cfg, device=DEV)
+    _say(f"route: 100M-token bank tiled, {off[-1]} rows")
+    _route_both_layouts(qr, kr, off, cfg.top_k, "100M tiled")
 
 
 # ==========================================================================
