@@ -217,8 +217,7 @@ def main():
     log(f"bank: {n_docs} docs, {bank_tokens} tokens, {n_pool} pooled rows")
     kr = synth.pooled_router_bank(cfg, lens, device=dev)
     lay = args.kr_layout
-    bank = synth.tile_router_bank(kr) if lay == "tiled" else kr      # what the scan reads
-    rkw = {"kr_layout": lay, "n_pool": n_pool}
+    bank, rkw = _router_bank(kr, n_pool, lay)      # what the scan reads
     host_kv = synth.pooled_content_bank(cfg, lens, device=dev, pin=True)
     pool_off_d = torch.as_tensor(pool_off, device=dev)
     pool_off_h = torch.as_tensor(pool_off)
@@ -404,10 +403,17 @@ class StreamEvents:
         return a.elapsed_time(b)
 
 
-def _supporting_line(metric, value, unit, workload, roofline, extra, higher=True):
+def _router_bank(kr, n_pool, lay):
+    """The router bank in the layout the scan reads, and route()'s keywords for it."""
+    return (synth.tile_router_bank(kr) if lay == "tiled" else kr), {"kr_layout": lay, "n_pool": n_pool}
+
+
+def _supporting_line(metric, value, unit, workload, roofline, extra, higher=True, kr_layout=None):
+    cfg = {"workload": workload}
+    if kr_layout:
+        cfg["kr_layout"] = kr_layout
     res = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "higher_is_better": higher,
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": {"workload": workload},
-           "roofline": roofline}
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg, "roofline": roofline}
     res.update(extra)
     print(json.dumps(res), flush=True)
 
@@ -424,7 +430,7 @@ def workload_interleave(args, dev):
     off = synth.row_offsets(lens, cfg.pool)
     n_docs, n_pool = len(lens), int(off[-1])
     log(f"interleave bank: {n_docs} docs, {int(lens.sum())} tokens, {n_pool} pooled rows")
-    kr = synth.pooled_router_bank(cfg, lens, device=dev)
+    kr, rkw = _router_bank(synth.pooled_router_bank(cfg, lens, device=dev), n_pool, args.kr_layout)
     host_kv = synth.pooled_content_bank(cfg, lens, device=dev, pin=True)
     off_d = torch.as_tensor(off, device=dev)
     k, B = cfg.top_k, cfg.batch
@@ -458,7 +464,7 @@ def workload_interleave(args, dev):
             if timed:
                 route_ev.pairs[i][0].record(stream)
             msa.route(qrs[r], kr, off_d, k, dsc, tki, tks, rws, assembly=asm, stream=stream,
-                      prof_events=scan_ev.pairs[i] if timed else None)
+                      prof_events=scan_ev.pairs[i] if timed else None, **rkw)
             if timed:
                 route_ev.pairs[i][1].record(stream)
                 dec_ev.pairs[i][0].record(stream)
@@ -501,10 +507,10 @@ def workload_interleave(args, dev):
         f"interleave-50M: {n_docs} docs, {int(lens.sum())} tokens (lognormal, mean 1024), {n_pool} pooled rows; "
         f"64 queries x {R} rounds of top-{k}, memory <= {mem_cap} rows + {cfg.local_len} local tokens, "
         "GQA 32/8 x 128",
-        {"kernel": "route bank scan, 64 one-token queries (scan_wide_kernel<8, 4, 4>)", "bound": "hbm",
+        {"kernel": f"route bank scan, 64 one-token queries (scan_wide_kernel<8, 4, 4>, {args.kr_layout} bank)", "bound": "hbm",
          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
          "traffic": None},
-        {"ms_per_round": float(round_ms), "rounds": per_round, "reps": reps})
+        {"ms_per_round": float(round_ms), "rounds": per_round, "reps": reps}, kr_layout=args.kr_layout)
 
 
 def workload_prefill(args, dev):
@@ -522,17 +528,20 @@ def workload_prefill(args, dev):
     log(f"prefill bank: {n_docs} docs, {n_tok} tokens, {n_pool} pooled rows")
     off_d = torch.as_tensor(off, device=dev)
     kv = torch.empty((n_pool, 2, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
-    krp = torch.empty((n_pool, cfg.n_router_heads, cfg.router_dim), dtype=torch.bfloat16, device=dev)
+    lay = args.kr_layout
+    rkw = {"kr_layout": lay, "n_pool": n_pool}
+    krp = torch.empty((msa.bank_rows(n_pool, lay), cfg.n_router_heads, cfg.router_dim), dtype=torch.bfloat16,
+                      device=dev)
     stream = torch.cuda.current_stream()
     reps = args.reps
     pool_ev = StreamEvents(reps)
     for _ in range(2):
         msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], off_d, cfg.pool, cfg.rope_theta,
-                        n_pool, kv, krp, stream=stream)
+                        n_pool, kv, krp, stream=stream, kr_layout=lay)
     for i in range(reps):
         pool_ev.pairs[i][0].record(stream)
         msa.pool_encode(bank["k"], bank["v"], bank["kr"], bank["doc_tok_off"], off_d, cfg.pool, cfg.rope_theta,
-                        n_pool, kv, krp, stream=stream)
+                        n_pool, kv, krp, stream=stream, kr_layout=lay)
         pool_ev.pairs[i][1].record(stream)
     torch.cuda.synchronize()
     pool_ms = np.mean([pool_ev.ms(i) for i in range(reps)])
@@ -565,7 +574,7 @@ def workload_prefill(args, dev):
         if i >= 0:
             route_ev.pairs[i][0].record(stream)
         msa.route(qr, krp, off_d, k, workspace=rws, assembly=asm, stream=stream,
-                  prof_events=scan_ev.pairs[i] if i >= 0 else None)
+                  prof_events=scan_ev.pairs[i] if i >= 0 else None, **rkw)
         if i >= 0:
             route_ev.pairs[i][1].record(stream)
             pre_ev.pairs[i][0].record(stream)
@@ -592,14 +601,14 @@ def workload_prefill(args, dev):
         {"kernel": "pool_kernel<bf16> (encode)", "bound": "hbm", "achieved": pool_gbs, "peak": HBM_PEAK_GBS,
          "unit": "GB/s", "frac": pool_gbs / HBM_PEAK_GBS, "traffic": None},
         {"encode_us": float(pool_ms * 1e3), "encode_bytes": pool_read + pool_write,
-         "routing": {"kernel": "scan_wide_kernel<8, 4, 4>", "bound": "mfma", "scan_us": float(scan_ms * 1e3),
+         "routing": {"kernel": f"scan_wide_kernel<8, 4, 4> ({args.kr_layout} bank)", "bound": "mfma", "scan_us": float(scan_ms * 1e3),
                      "achieved_TFs": tfs, "peak_TFs": 2500.0, "frac": tfs / 2500.0, "bank": "MALL-warm (44.6 MB)",
                      "route_us": float(np.mean([route_ev.ms(i) for i in range(reps)]) * 1e3)},
          "prefill_attention": {"kernel": "attend_kernel<128> (256 tokens, causal, GQA 32/8)", "bound": "mfma",
                                "memory_rows": mrows, "attend_us": float(att_ms * 1e3),
                                "achieved_TFs": att_flops / (att_ms / 1e3) / 1e12,
                                "with_merge_us": float(np.mean([pre_ev.ms(i) for i in range(reps)]) * 1e3)},
-         "decode_us": float(np.mean([dec_ev.ms(i) for i in range(reps)]) * 1e3), "reps": reps})
+         "decode_us": float(np.mean([dec_ev.ms(i) for i in range(reps)]) * 1e3), "reps": reps}, kr_layout=args.kr_layout)
 
 
 def workload_needles(args, dev):
@@ -614,6 +623,7 @@ def workload_needles(args, dev):
     kr = synth.pooled_router_bank(cfg, lens, device=dev)
     qr = synth.router_queries(cfg, device=dev)
     needles = synth.plant_needles(cfg, qr, kr, off)
+    kr, rkw = _router_bank(kr, n_pool, args.kr_layout)
     off_d = torch.as_tensor(off, device=dev)
     k = cfg.top_k
     rws = torch.empty(msa.route_workspace_bytes(torch.bfloat16, cfg.batch, 1, cfg.n_router_heads, cfg.router_dim,
@@ -626,7 +636,7 @@ def workload_needles(args, dev):
         if i >= 0:
             route_ev.pairs[i][0].record(stream)
         idx, _, _ = msa.route(qr, kr, off_d, k, workspace=rws, stream=stream,
-                              prof_events=scan_ev.pairs[i] if i >= 0 else None)
+                              prof_events=scan_ev.pairs[i] if i >= 0 else None, **rkw)
         if i >= 0:
             route_ev.pairs[i][1].record(stream)
     torch.cuda.synchronize()
@@ -640,11 +650,11 @@ def workload_needles(args, dev):
         "bank tokens/s",
         f"needles-16M: {n_docs} docs, {int(lens.sum())} tokens (lognormal, mean 512), {n_pool} pooled rows, "
         "8 one-token queries, top-16",
-        {"kernel": "route bank scan, 8 one-token queries (scan_mfma_kernel<8, 4, 1>)", "bound": "hbm",
+        {"kernel": f"route bank scan, 8 one-token queries (scan_mfma_kernel<8, 4, 1>, {args.kr_layout} bank)", "bound": "hbm",
          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
          "traffic": None},
         {"scan_us": float(scan_ms * 1e3), "route_us": float(route_ms * 1e3), "needle_recall_top16": found,
-         "reps": reps})
+         "reps": reps}, kr_layout=args.kr_layout)
 
 
 def workload_encode(args, dev):
@@ -666,7 +676,9 @@ def workload_encode(args, dev):
     tok_off_h = synth.token_offsets(bank["lens"])
     log(f"encode: {n_docs} docs, {n_tok} tokens -> {n_pool} rows, batches of {per} docs")
     tier = torch.empty((n_pool, 2, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, pin_memory=True)
-    kr_bank = torch.empty((n_pool, cfg.n_router_heads, cfg.router_dim), dtype=torch.bfloat16, device=dev)
+    lay = args.kr_layout
+    kr_bank = torch.empty((msa.bank_rows(n_pool, lay), cfg.n_router_heads, cfg.router_dim), dtype=torch.bfloat16,
+                          device=dev)
     stage = torch.empty((int(boff[-1]), 2, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
     batches = []
     for d0 in range(0, n_docs, per):
@@ -680,7 +692,7 @@ def workload_encode(args, dev):
         for r0, nd, nt, npb, toff, poff in batches:
             kv_out = tier[r0:r0 + npb] if to_host else stage[:npb]
             msa.pool_encode(bank["k"][:nt], bank["v"][:nt], bank["kr"][:nt], toff, poff, cfg.pool, cfg.rope_theta,
-                            npb, kv_out, kr_bank[r0:r0 + npb], stream=stream)
+                            npb, kv_out, kr_bank, stream=stream, kr_layout=lay, kr_row_base=r0)
 
     res = {}
     for name, to_host in (("host_tier", True), ("hbm", False)):
@@ -703,13 +715,13 @@ def workload_encode(args, dev):
         "bank tokens encoded/s into the host tier (streaming encode)", n_tok / t_host, "tokens/s",
         f"encode-100M: {n_docs} docs x 512 tokens = {n_tok} tokens -> {n_pool} pooled rows in {len(batches)} batches "
         f"of {per} docs; pooled K/V (8x128 bf16, {host_bytes / 1e9:.2f} GB) into pinned host memory, pooled Kr into "
-        "HBM",
+        f"the HBM bank ({lay} layout, each batch at its first row)",
         {"kernel": "pool_kernel<bf16> (encode, K/V written over the host link)", "bound": "hbm",
          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
          "traffic": None},
         {"ms_total_host_tier": res["host_tier"], "ms_total_kv_to_hbm": res["hbm"],
          "host_link_GBs": host_bytes / t_host / 1e9, "tokens_per_s_kv_to_hbm": n_tok / (res["hbm"] / 1e3),
-         "batches": len(batches), "reps": max(1, args.reps // 5)})
+         "batches": len(batches), "reps": max(1, args.reps // 5)}, kr_layout=args.kr_layout)
 
 
 WORKLOADS = {"bank-100M": None, "encode-100M": workload_encode, "interleave-50M": workload_interleave, "prefill-1M": workload_prefill,
