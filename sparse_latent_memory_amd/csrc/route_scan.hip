@@ -46,8 +46,8 @@ constexpr int kWaves = 4;   // waves per workgroup
 #ifndef MSA_SCAN_NT        // 1: non-temporal bank loads (the bank is read once per call)
 #define MSA_SCAN_NT 0
 #endif
-#ifndef MSA_SCAN_CHUNKED   // 1: contiguous tile range per wave; 0: tiles strided over waves
-#define MSA_SCAN_CHUNKED 0
+#ifndef MSA_SCAN_BUF       // tiles whose row scores a wave keeps in LDS before storing them in one
+#define MSA_SCAN_BUF 16       //   burst (0: store after every tile)
 #endif
 #ifndef MSA_SCAN_GRID_MULT // workgroups launched per resident workgroup slot
 #define MSA_SCAN_GRID_MULT 1
@@ -79,6 +79,9 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
   constexpr int GF = HG * KS;                     // fragments per head group
   __shared__ u32x4 afrag[NF * 64];
   __shared__ float qscale[8 * HR];
+#if MSA_SCAN_BUF
+  __shared__ float rbuf_all[kWaves * MSA_SCAN_BUF * 8 * 16];
+#endif
   const int M = B * Tq;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
@@ -119,15 +122,16 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
   const int diag_src = ((col >> 2) << 4) + col;    // lane holding Gram[col][col]
   const int64_t n_tiles = (n_pool + 15) >> 4;
 
-#if MSA_SCAN_CHUNKED
-  // each wave streams one contiguous run of tiles
-  const int64_t n_waves = (int64_t)gridDim.x * kWaves, wid = (int64_t)blockIdx.x * kWaves + wave;
-  const int64_t t_begin = n_tiles * wid / n_waves, t_end = n_tiles * (wid + 1) / n_waves;
-  for (int64_t tile = t_begin; tile < t_end; ++tile) {
-#else
-  for (int64_t tile = (int64_t)blockIdx.x * kWaves + wave; tile < n_tiles;
-       tile += (int64_t)gridDim.x * kWaves) {
+  const int64_t t_step = (int64_t)gridDim.x * kWaves;
+#if MSA_SCAN_BUF
+  // Row scores wait in LDS and go out in bursts of MSA_SCAN_BUF tiles: a store
+  // after every tile (64 bytes per query) measured 1-6% slower (B = 1-8);
+  // issuing the burst behind the next tile's first loads measured slower
+  // still, as did storing in the order a wave produces the scores.
+  float *rbuf = rbuf_all + wave * (MSA_SCAN_BUF * 8 * 16);   // [slot][query][row in tile]
+  int n_buf = 0;
 #endif
+  for (int64_t tile = (int64_t)blockIdx.x * kWaves + wave; tile < n_tiles; tile += t_step) {
     const int64_t row = tile * 16 + col;
     // fragment f of this lane at rp + FS * f (the tiled bank holds whole
     // tiles; the row-major one is clamped to its last row)
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
       ts[2 * q] = __shfl(sc0, col + 16 * q, 64);
       ts[2 * q + 1] = __shfl(sc1, col + 16 * q, 64);
     }
-    if (grp == 0 && row < n_pool) {
+    if (grp == 0) {
       for (int b = 0; b < B; ++b) {
         float m = -INFINITY;
         for (int t = 0; t < Tq; ++t) {
@@ -196,9 +200,27 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
           for (int q = 1; q < 8; ++q) v = slot == q ? ts[q] : v;
           m = fmaxf(m, v);
         }
-        row_score[(int64_t)b * n_pool + row] = m;
+#if MSA_SCAN_BUF
+        rbuf[(n_buf * 8 + b) * 16 + col] = m;
+#else
+        if (row < n_pool) row_score[(int64_t)b * n_pool + row] = m;
+#endif
       }
     }
+#if MSA_SCAN_BUF
+    // flush when the buffer is full or this was the wave's last tile: slot j
+    // holds tile (tile - (n_buf - 1 - j) * t_step); the 64 lanes store four
+    // (slot, query) pieces of 16 rows per instruction
+    ++n_buf;
+    if (n_buf == MSA_SCAN_BUF || tile + t_step >= n_tiles) {
+      for (int idx = grp; idx < n_buf * B; idx += 4) {
+        const int j = idx / B, b = idx - j * B;
+        const int64_t r = (tile - (int64_t)(n_buf - 1 - j) * t_step) * 16 + col;
+        if (r < n_pool) row_score[(int64_t)b * n_pool + r] = rbuf[(j * 8 + b) * 16 + col];
+      }
+      n_buf = 0;
+    }
+#endif
   }
 }
 
