@@ -78,7 +78,7 @@ def calibrate_copy():
     print(json.dumps({"calibration_copy_bytes": CALIBRATION_BYTES, "launches": 3}), flush=True)
 
 
-SCAN_KERNELS = {"tiled": "scan_mfma_kernel<8, 4, 1, true>", "rows": "scan_mfma_kernel<8, 4, 1, false>"}
+SCAN_KERNELS = {"tiled": "scan_mfma_kernel<8, 4, 1, true, true>", "rows": "scan_mfma_kernel<8, 4, 1, false, true>"}
 SCAN_KERNEL = SCAN_KERNELS["tiled"]     # the headline line's router bank is tiled
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -650,7 +650,8 @@ def workload_needles(args, dev):
         "bank tokens/s",
         f"needles-16M: {n_docs} docs, {int(lens.sum())} tokens (lognormal, mean 512), {n_pool} pooled rows, "
         "8 one-token queries, top-16",
-        {"kernel": f"route bank scan, 8 one-token queries (scan_mfma_kernel<8, 4, 1>, {args.kr_layout} bank)", "bound": "hbm",
+        {"kernel": "route bank scan, 8 one-token queries (scan_mfma_kernel<8, 4, 1, "
+                   f"{'true' if args.kr_layout == 'tiled' else 'false'}, true>)", "bound": "hbm",
          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
          "traffic": None},
         {"scan_us": float(scan_ms * 1e3), "route_us": float(route_ms * 1e3), "needle_recall_top16": found,

@@ -33,19 +33,28 @@ struct GatherPlan {
 };
 
 struct RouteWs {  // carved out of the caller's workspace
+  // row path (narrow scan, VALU scan, wide scan with several tokens per query)
   float *row_score;        // [B, n_parts, n_pool]
+  // document path (one token per query, matrix-core scans): the scan reduces
+  // every 16-row tile per document itself
+  float *doc_part;         // [n_docs, qstride] max over a document's rows in the tile where it starts
+  float *tile_cont;        // [n_tiles, qstride] max over a tile's first rows when they continue a document
+  int32_t *tile_doc;       // [n_tiles] document holding the tile's first row
+  uint32_t *tile_bits;     // [n_tiles] bit r: row 16 t + r starts a document (or is row n_pool)
   float *qhat;             // [B*Tq, Hr*dr] fp32 unit queries (VALU and wide scans)
   u32x4 *wide_frag;        // [n_mt, Hr*dr/32, 64] bf16 query fragments (wide scan)
-  uint64_t *cand;          // [B, n_blocks, cand_per_block]
+  uint64_t *blockmax;      // [B, n_blocks] best document key per block of kDocsPerBlock documents
   GatherPlan *plan;        // [B, k]
-  int32_t n_blocks;        // document blocks of the partial top-k
-  int32_t cand_per_block;
+  int32_t n_blocks;        // blocks of kDocsPerBlock documents
   int32_t n_parts;         // partial token maxima per query in row_score (wide scan), else 1
+  int32_t qstride;         // query stride of doc_part / tile_cont: a multiple of 16 on the wide
+                           // scan, B rounded up to 4 on the narrow one; 0 on the row path
 };
 // Routing kernels.  The bank scan writes row_score[b, j] (max over query b's
-// tokens of the head-mean cosine); selection reduces it per document, takes
-// the exact top-k and plans/performs the device-side assembly.
-constexpr int kDocsPerBlock = 256;    // documents per partial top-k block
+// tokens of the head-mean cosine) or, on the document path, per-document
+// parts of each tile; selection reduces them per document, takes the exact
+// top-k and plans/performs the device-side assembly.
+constexpr int kDocsPerBlock = 256;    // documents per block of the top-k bound
 
 // v_mfma_f32_16x16x32_bf16 scan shapes: router dim 64 or 128, heads a power
 // of two up to 8 (16 with dim 64)
@@ -111,15 +120,17 @@ __host__ __device__ inline void wide_chunk(const WideLayout &L, int c, int *t0, 
   }
 }
 // bf16, at most 8 query tokens (route_scan.hip)
-hipError_t launch_scan_narrow(const msa_route_args &a, float *row_score, hipStream_t s);
+hipError_t launch_scan_narrow(const msa_route_args &a, const RouteWs &ws, hipStream_t s);
 // fp32 unit queries (route_scan_wide.hip)
 hipError_t launch_prep_unit(const msa_route_args &a, float *qhat, hipStream_t s);
 // bf16 query fragments and the MFMA scan for more than 8 tokens
 hipError_t launch_prep_wide(const msa_route_args &a, const float *qhat, u32x4 *frag, hipStream_t s);
-hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s);
+hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, const RouteWs &ws, hipStream_t s);
 // fp32 (any token count): one wave per bank row
 hipError_t launch_scan_valu(const msa_route_args &a, const float *qhat, float *row_score, hipStream_t s);
-// per-document max, exact top-k, assembly plan and device-side gather (route_select.hip)
+// document map of the document path, per-document scores, exact top-k,
+// assembly plan and device-side gather (route_select.hip)
+hipError_t launch_doc_map(const msa_route_args &a, const RouteWs &ws, hipStream_t s);
 hipError_t launch_select(const msa_route_args &a, const RouteWs &ws, const void *host_kv_dev, hipStream_t s);
 
 size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t hr, int32_t dr,

@@ -20,6 +20,10 @@
 
 #include <algorithm>
 
+#ifndef MSA_ROUTE_NARROW_DOCS   // 1: one-token batches of up to 8 queries also take the document path
+#define MSA_ROUTE_NARROW_DOCS 1
+#endif
+
 namespace msa {
 namespace {
 
@@ -47,31 +51,45 @@ size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t h
                        int64_t n_pool, int32_t top_k, void *base, RouteWs *ws) {
   const int32_t M = batch * q_tokens;
   const int32_t n_blocks = (n_docs + kDocsPerBlock - 1) / kDocsPerBlock;
-  const int32_t cpb = std::min(top_k, kDocsPerBlock);
-  const int32_t n_parts =
-      wide_path(dtype, M, hr, dr) ? wide_layout(batch, q_tokens, wide_mg(hr * dr / 32, dr / 32)).n_parts : 1;
+  const bool wide = wide_path(dtype, M, hr, dr);
+  const bool narrow = narrow_path(dtype, M, hr, dr);
+  const bool docs = (wide || (narrow && MSA_ROUTE_NARROW_DOCS)) && q_tokens == 1;   // the document path
+  const int32_t n_parts = wide ? wide_layout(batch, q_tokens, wide_mg(hr * dr / 32, dr / 32)).n_parts : 1;
+  const int64_t n_tiles = (n_pool + 15) / 16;
+  const int32_t qstride = !docs ? 0 : wide ? wide_tiles(batch, 1) * 16 : (batch + 3) / 4 * 4;
   size_t off = 0;
   const size_t o_rs = off;
-  off = align256(off + sizeof(float) * (size_t)batch * n_parts * (size_t)n_pool);
+  if (!docs) off = align256(off + sizeof(float) * (size_t)batch * n_parts * (size_t)n_pool);
+  const size_t o_dp = off;
+  off = align256(off + sizeof(float) * (size_t)n_docs * qstride);
+  const size_t o_tc = off;
+  off = align256(off + sizeof(float) * (size_t)n_tiles * qstride);
+  const size_t o_td = off;
+  if (docs) off = align256(off + sizeof(int32_t) * (size_t)n_tiles);
+  const size_t o_tb = off;
+  if (docs) off = align256(off + sizeof(uint32_t) * (size_t)n_tiles);
   const size_t o_q = off;
   if (!narrow_path(dtype, M, hr, dr)) off = align256(off + sizeof(float) * (size_t)M * hr * dr);
   const size_t o_w = off;
-  if (wide_path(dtype, M, hr, dr))
-    off = align256(off + sizeof(u32x4) * 64 * (size_t)hr * (dr / 32) * wide_tiles(batch, q_tokens));
-  const size_t o_c = off;
-  off = align256(off + sizeof(uint64_t) * (size_t)batch * n_blocks * cpb);
+  if (wide) off = align256(off + sizeof(u32x4) * 64 * (size_t)hr * (dr / 32) * wide_tiles(batch, q_tokens));
+  const size_t o_bm = off;
+  off = align256(off + sizeof(uint64_t) * (size_t)batch * n_blocks);
   const size_t o_plan = off;
   off = align256(off + sizeof(GatherPlan) * (size_t)batch * top_k);
   if (ws) {
     char *p = reinterpret_cast<char *>(base);
     ws->row_score = reinterpret_cast<float *>(p + o_rs);
+    ws->doc_part = reinterpret_cast<float *>(p + o_dp);
+    ws->tile_cont = reinterpret_cast<float *>(p + o_tc);
+    ws->tile_doc = reinterpret_cast<int32_t *>(p + o_td);
+    ws->tile_bits = reinterpret_cast<uint32_t *>(p + o_tb);
     ws->qhat = reinterpret_cast<float *>(p + o_q);
     ws->wide_frag = reinterpret_cast<u32x4 *>(p + o_w);
-    ws->cand = reinterpret_cast<uint64_t *>(p + o_c);
+    ws->blockmax = reinterpret_cast<uint64_t *>(p + o_bm);
     ws->plan = reinterpret_cast<GatherPlan *>(p + o_plan);
     ws->n_blocks = n_blocks;
-    ws->cand_per_block = cpb;
     ws->n_parts = n_parts;
+    ws->qstride = qstride;
   }
   return off;
 }
@@ -81,12 +99,14 @@ hipError_t launch_route(const msa_route_args &a, const RouteWs &ws, const void *
   hipError_t e = hipSuccess;
   // the scan launchers attach a.prof_event_begin / _end to the scan kernel
   if (narrow_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
-    e = launch_scan_narrow(a, ws.row_score, s);
+    if (ws.qstride > 0 && (e = launch_doc_map(a, ws, s)) != hipSuccess) return e;
+    e = launch_scan_narrow(a, ws, s);
   } else {
     if ((e = launch_prep_unit(a, ws.qhat, s)) != hipSuccess) return e;
     if (wide_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
       if ((e = launch_prep_wide(a, ws.qhat, ws.wide_frag, s)) != hipSuccess) return e;
-      e = launch_scan_wide(a, ws.wide_frag, ws.row_score, s);
+      if (ws.qstride > 0 && (e = launch_doc_map(a, ws, s)) != hipSuccess) return e;
+      e = launch_scan_wide(a, ws.wide_frag, ws, s);
     } else {
       e = launch_scan_valu(a, ws.qhat, ws.row_score, s);
     }

@@ -67,11 +67,16 @@ __device__ __forceinline__ u32x4 scan_ld(const uint16_t *p) {
   else return SCAN_LD(p);
 }
 
-template <int HR, int KS, int HG, bool TILED>
-__global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restrict__ kr,
-                                                        const uint16_t *__restrict__ qr,
-                                                        float *__restrict__ row_score, int64_t n_pool, int B,
-                                                        int Tq) {
+// DOCS (one token per query, the document path): instead of B scores per
+// bank row the epilogue writes, per tile, the max over each run of rows that
+// belongs to one document (a segmented max over the tile's 16 rows, runs
+// marked by the document map): doc_part[d] for the document starting in the
+// tile, tile_cont[tile] for rows continuing an earlier document.
+template <int HR, int KS, int HG, bool TILED, bool DOCS>
+__global__ __launch_bounds__(256) void scan_mfma_kernel(
+    const uint16_t *__restrict__ kr, const uint16_t *__restrict__ qr, float *__restrict__ row_score,
+    const int32_t *__restrict__ tile_doc, const uint32_t *__restrict__ tile_bits, float *__restrict__ doc_part,
+    float *__restrict__ tile_cont, int qs, int n_docs, int64_t n_pool, int B, int Tq) {
   constexpr int NF = HR * KS;                     // fragments per 16-row tile per lane
   constexpr int DR = KS * 32;                     // router head dim
   constexpr int ROW = HR * DR;                    // elements per bank row
@@ -146,6 +151,12 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
     u32x4 cur[GF];
 #pragma unroll
     for (int f = 0; f < GF; ++f) cur[f] = scan_ld<TILED>(rp + FS * f);
+    uint32_t bits = 0;                     // the tile's document map, used at its end
+    int32_t tdoc = 0;
+    if constexpr (DOCS) {
+      bits = tile_bits[tile];
+      tdoc = tile_doc[tile];
+    }
 
     float sc0 = 0.f, sc1 = 0.f;
 #if MSA_SCAN_PIPE
@@ -190,7 +201,30 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
       ts[2 * q] = __shfl(sc0, col + 16 * q, 64);
       ts[2 * q + 1] = __shfl(sc1, col + 16 * q, 64);
     }
-    if (grp == 0) {
+    if constexpr (DOCS) {
+      // query b's score of row col is ts[b]; runs: doubling steps within the
+      // 16 lanes of a group, each taken only while no document starts between
+      const bool run_start = col == 0 || ((bits >> col) & 1u);
+      const bool starts_doc = (bits >> col) & 1u;
+      int d = tdoc + __popc(bits & ((2u << col) - 2u));   // clamped: bad offsets give wrong numbers only
+      d = d < 0 ? 0 : (d >= n_docs ? n_docs - 1 : d);
+#pragma unroll
+      for (int sh = 1; sh < 16; sh <<= 1) {
+        const bool same = col + sh < 16 && ((bits >> (col + 1)) & ((1u << sh) - 1u)) == 0u;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          if (b < B) {
+            const float u = __shfl_down(ts[b], sh, 16);
+            ts[b] = same ? fmaxf(ts[b], u) : ts[b];
+          }
+        }
+      }
+      if (grp == 0 && run_start && row < n_pool) {
+        float *dst = starts_doc ? doc_part + (int64_t)d * qs : tile_cont + tile * qs;
+        *reinterpret_cast<f32x4 *>(dst) = f32x4{ts[0], ts[1], ts[2], ts[3]};
+        if (qs > 4) *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{ts[4], ts[5], ts[6], ts[7]};
+      }
+    } else if (grp == 0) {
       for (int b = 0; b < B; ++b) {
         float m = -INFINITY;
         for (int t = 0; t < Tq; ++t) {
@@ -211,8 +245,8 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
     // flush when the buffer is full or this was the wave's last tile: slot j
     // holds tile (tile - (n_buf - 1 - j) * t_step); the 64 lanes store four
     // (slot, query) pieces of 16 rows per instruction
-    ++n_buf;
-    if (n_buf == MSA_SCAN_BUF || tile + t_step >= n_tiles) {
+    if constexpr (!DOCS) ++n_buf;
+    if (!DOCS && (n_buf == MSA_SCAN_BUF || tile + t_step >= n_tiles)) {
       for (int idx = grp; idx < n_buf * B; idx += 4) {
         const int j = idx / B, b = idx - j * B;
         const int64_t r = (tile - (int64_t)(n_buf - 1 - j) * t_step) * 16 + col;
@@ -224,45 +258,48 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t *__restri
   }
 }
 
-template <int HR, int KS, bool TILED>
-hipError_t launch_scan_mfma_t(const msa_route_args &a, float *row_score, hipStream_t s) {
+template <int HR, int KS, bool TILED, bool DOCS>
+hipError_t launch_scan_mfma_t(const msa_route_args &a, const RouteWs &ws, hipStream_t s) {
   constexpr int HG = HR < MSA_SCAN_HG ? HR : MSA_SCAN_HG;
   const int64_t n_tiles = (a.n_pool + 15) / 16;
   int occ = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_mfma_kernel<HR, KS, HG, TILED>, 256, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_mfma_kernel<HR, KS, HG, TILED, DOCS>, 256, 0) !=
           hipSuccess ||
       occ < 1)
     occ = 1;
   const int64_t want = (int64_t)device_info().n_cu * occ * MSA_SCAN_GRID_MULT;
   const int64_t need = (n_tiles + kWaves - 1) / kWaves;
   const int grid = (int)std::max<int64_t>(1, std::min(want, need));
-  hipExtLaunchKernelGGL((scan_mfma_kernel<HR, KS, HG, TILED>), dim3(grid), dim3(256), 0, s,
+  hipExtLaunchKernelGGL((scan_mfma_kernel<HR, KS, HG, TILED, DOCS>), dim3(grid), dim3(256), 0, s,
                         prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
                         reinterpret_cast<const uint16_t *>(a.kr_pooled), reinterpret_cast<const uint16_t *>(a.qr),
-                        row_score, a.n_pool, a.batch, a.q_tokens);
+                        ws.row_score, ws.tile_doc, ws.tile_bits, ws.doc_part, ws.tile_cont, ws.qstride, a.n_docs,
+                        a.n_pool, a.batch, a.q_tokens);
   return hipGetLastError();
 }
 
 template <int HR, int KS>
-hipError_t launch_scan_mfma(const msa_route_args &a, float *row_score, hipStream_t s) {
-  return a.kr_layout == MSA_KR_TILED ? launch_scan_mfma_t<HR, KS, true>(a, row_score, s)
-                                     : launch_scan_mfma_t<HR, KS, false>(a, row_score, s);
+hipError_t launch_scan_mfma(const msa_route_args &a, const RouteWs &ws, hipStream_t s) {
+  const bool docs = ws.qstride > 0;
+  if (a.kr_layout == MSA_KR_TILED)
+    return docs ? launch_scan_mfma_t<HR, KS, true, true>(a, ws, s) : launch_scan_mfma_t<HR, KS, true, false>(a, ws, s);
+  return docs ? launch_scan_mfma_t<HR, KS, false, true>(a, ws, s) : launch_scan_mfma_t<HR, KS, false, false>(a, ws, s);
 }
 
 }  // namespace
 
-hipError_t launch_scan_narrow(const msa_route_args &a, float *row_score, hipStream_t s) {
+hipError_t launch_scan_narrow(const msa_route_args &a, const RouteWs &ws, hipStream_t s) {
   const int ks = a.router_dim / 32;
   switch (a.n_router_heads * 8 + ks) {
-    case 1 * 8 + 2: return launch_scan_mfma<1, 2>(a, row_score, s);
-    case 1 * 8 + 4: return launch_scan_mfma<1, 4>(a, row_score, s);
-    case 2 * 8 + 2: return launch_scan_mfma<2, 2>(a, row_score, s);
-    case 2 * 8 + 4: return launch_scan_mfma<2, 4>(a, row_score, s);
-    case 4 * 8 + 2: return launch_scan_mfma<4, 2>(a, row_score, s);
-    case 4 * 8 + 4: return launch_scan_mfma<4, 4>(a, row_score, s);
-    case 8 * 8 + 2: return launch_scan_mfma<8, 2>(a, row_score, s);
-    case 8 * 8 + 4: return launch_scan_mfma<8, 4>(a, row_score, s);
-    case 16 * 8 + 2: return launch_scan_mfma<16, 2>(a, row_score, s);
+    case 1 * 8 + 2: return launch_scan_mfma<1, 2>(a, ws, s);
+    case 1 * 8 + 4: return launch_scan_mfma<1, 4>(a, ws, s);
+    case 2 * 8 + 2: return launch_scan_mfma<2, 2>(a, ws, s);
+    case 2 * 8 + 4: return launch_scan_mfma<2, 4>(a, ws, s);
+    case 4 * 8 + 2: return launch_scan_mfma<4, 2>(a, ws, s);
+    case 4 * 8 + 4: return launch_scan_mfma<4, 4>(a, ws, s);
+    case 8 * 8 + 2: return launch_scan_mfma<8, 2>(a, ws, s);
+    case 8 * 8 + 4: return launch_scan_mfma<8, 4>(a, ws, s);
+    case 16 * 8 + 2: return launch_scan_mfma<16, 2>(a, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

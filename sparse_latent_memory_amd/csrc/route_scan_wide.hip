@@ -99,11 +99,17 @@ constexpr int kWideWaves = 8;
 // 16-64 queries, and twice as slow when chunks share tiles).
 enum WideBank { kWideRows = 0, kWideTiled = 1, kWideTiledNT = 2 };
 
+// One token per query (the document path): instead of B scores per bank row
+// the epilogue writes, per tile and query, the max over each run of rows
+// that belongs to one document (a segmented max over the tile's 16 rows,
+// runs marked by the document map): doc_part[d] for the document starting
+// in the tile, tile_cont[tile] for rows continuing an earlier document.
+// Storing B scores per row cost a third of the scan at 64 queries.
 template <int HR, int KS, int NM, int BANK>
-__global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(const uint16_t *__restrict__ kr,
-                                                                    const u32x4 *__restrict__ frag,
-                                                                    float *__restrict__ row_score, int64_t n_pool,
-                                                                    int B, int Tq) {
+__global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
+    const uint16_t *__restrict__ kr, const u32x4 *__restrict__ frag, float *__restrict__ row_score,
+    const int32_t *__restrict__ tile_doc, const uint32_t *__restrict__ tile_bits, float *__restrict__ doc_part,
+    float *__restrict__ tile_cont, int qstride, int n_docs, int64_t n_pool, int B, int Tq) {
   constexpr int NF = HR * KS;
   constexpr int ROW = NF * 32;
   static_assert(NM <= wide_mg(NF, KS), "query chunk exceeds the LDS budget");
@@ -184,20 +190,43 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(const uint16
     for (int mt = 0; mt < NM; ++mt) acc[mt] += d[mt] * inv;
   };
 
-  // row scores of one bank tile: Tq == 1 stores every query's score; Tq > 1
-  // stores per query the max over the chunk's tiles of that query
-  auto epilogue = [&](int t0, int nm, int part, int64_t row, const f32x4 *acc) {
-    if (L.tok1) {
-      // rows 4*grp + i of tile t are queries 16 t + 4 grp + i
+  // Document path (Tq == 1): lane (col, grp) holds, for bank row col of the
+  // tile, the scores of queries 16 (t0 + mt) + 4 grp + i in acc[mt][i].
+  // After the segmented max (doubling steps within the 16 lanes of a group,
+  // each taken only while no document starts in between), a lane whose row
+  // starts a run holds the run's max and stores its 4 queries at once.
+  auto epilogue_docs = [&](int t0, int nm, int64_t tile, uint32_t bits, int32_t tdoc, const f32x4 *acc) {
+    const int64_t row = tile * 16 + col;
+    const bool run_start = col == 0 || ((bits >> col) & 1u);
+    const bool starts_doc = (bits >> col) & 1u;
+    // document of a run that starts here: the tile's first document plus the
+    // starts in rows 1..col (clamped: bad offsets give wrong numbers only)
+    int d = tdoc + __popc(bits & ((2u << col) - 2u));
+    d = d < 0 ? 0 : (d >= n_docs ? n_docs - 1 : d);
 #pragma unroll
-      for (int mt = 0; mt < NM; ++mt) {
+    for (int mt = 0; mt < NM; ++mt) {
+      if (mt >= nm) break;                // (uniform)
+      f32x4 v = acc[mt];
+#pragma unroll
+      for (int sh = 1; sh < 16; sh <<= 1) {
+        const bool same = col + sh < 16 && ((bits >> (col + 1)) & ((1u << sh) - 1u)) == 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int b = (t0 + mt) * 16 + 4 * grp + i;
-          if (mt < nm && b < B) row_score[(int64_t)b * n_pool + row] = acc[mt][i];
+          const float u = __shfl_down(v[i], sh, 16);
+          v[i] = same ? fmaxf(v[i], u) : v[i];
         }
       }
-    } else {
+      if (run_start && row < n_pool) {
+        const int b0 = (t0 + mt) * 16 + 4 * grp;
+        float *dst = starts_doc ? doc_part + (int64_t)d * qstride + b0 : tile_cont + tile * qstride + b0;
+        *reinterpret_cast<f32x4 *>(dst) = v;
+      }
+    }
+  };
+  // row scores of one bank tile (Tq > 1): per query the max over the
+  // chunk's tiles of that query
+  auto epilogue = [&](int t0, int nm, int part, int64_t row, const f32x4 *acc) {
+    {
       float qmax = -INFINITY;         // max over the chunk's tiles of one query
 #pragma unroll
       for (int mt = 0; mt < NM; ++mt) {
@@ -227,7 +256,16 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(const uint16
     u32x4 fa[KS], fb[KS];
     load(stream, 0, fa);
     for (int64_t g = stream; g < n_groups; g += S) {
-      const int64_t row = (g * kWideWaves + wave) * 16 + col;
+      const int64_t tile = g * kWideWaves + wave;
+      const int64_t row = tile * 16 + col;
+      // the tile's document map (document path), requested ahead of its use
+      uint32_t bits = 0;
+      int32_t tdoc = 0;
+      if (L.tok1) {
+        const int64_t tc = tile < n_tiles ? tile : n_tiles - 1;
+        bits = tile_bits[tc];
+        tdoc = tile_doc[tc];
+      }
       f32x4 acc[NM];
 #pragma unroll
       for (int mt = 0; mt < NM; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -250,7 +288,11 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(const uint16
           head(h + 1, fb, acc);
         }
       }
-      if (row < n_pool) epilogue(t0, nm, part, row, acc);
+      if (L.tok1) {
+        if (tile < n_tiles) epilogue_docs(t0, nm, tile, bits, tdoc, acc);   // (wave-uniform)
+      } else if (row < n_pool) {
+        epilogue(t0, nm, part, row, acc);
+      }
     }
   }
 }
@@ -291,28 +333,29 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const T *__restrict__ kr
 }
 
 template <int HR, int KS, int NM, int BANK>
-void launch_wide_bank(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s) {
+void launch_wide_bank(const msa_route_args &a, const u32x4 *frag, const RouteWs &ws, hipStream_t s) {
   // one workgroup per CU (the query chunk takes most of the LDS)
   hipExtLaunchKernelGGL((scan_wide_kernel<HR, KS, NM, BANK>), dim3(device_info().n_cu), dim3(kWideWaves * 64), 0,
                         s, prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
-                        reinterpret_cast<const uint16_t *>(a.kr_pooled), frag, row_score, a.n_pool, a.batch,
+                        reinterpret_cast<const uint16_t *>(a.kr_pooled), frag, ws.row_score, ws.tile_doc,
+                        ws.tile_bits, ws.doc_part, ws.tile_cont, ws.qstride, a.n_docs, a.n_pool, a.batch,
                         a.q_tokens);
 }
 
 template <int HR, int KS, int NM>
-hipError_t launch_wide_nm(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s) {
+hipError_t launch_wide_nm(const msa_route_args &a, const u32x4 *frag, const RouteWs &ws, hipStream_t s) {
   if (a.kr_layout != MSA_KR_TILED)
-    launch_wide_bank<HR, KS, NM, kWideRows>(a, frag, row_score, s);
+    launch_wide_bank<HR, KS, NM, kWideRows>(a, frag, ws, s);
   else if (wide_layout(a.batch, a.q_tokens, wide_mg(HR * KS, KS)).n_chunks == 1)
-    launch_wide_bank<HR, KS, NM, kWideTiledNT>(a, frag, row_score, s);
+    launch_wide_bank<HR, KS, NM, kWideTiledNT>(a, frag, ws, s);
   else
-    launch_wide_bank<HR, KS, NM, kWideTiled>(a, frag, row_score, s);
+    launch_wide_bank<HR, KS, NM, kWideTiled>(a, frag, ws, s);
   return hipGetLastError();
 }
 
 // NM = the largest chunk, rounded up to a power of two (at most the LDS budget)
 template <int HR, int KS>
-hipError_t launch_wide_t(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s) {
+hipError_t launch_wide_t(const msa_route_args &a, const u32x4 *frag, const RouteWs &ws, hipStream_t s) {
   constexpr int MG = wide_mg(HR * KS, KS);
   const WideLayout L = wide_layout(a.batch, a.q_tokens, MG);
   int need = 0;
@@ -321,10 +364,10 @@ hipError_t launch_wide_t(const msa_route_args &a, const u32x4 *frag, float *row_
     wide_chunk(L, c, &t0, &t1);
     need = std::max(need, t1 - t0);
   }
-  if (need <= 1) return launch_wide_nm<HR, KS, 1>(a, frag, row_score, s);
-  if (need <= 2 || MG < 4) return launch_wide_nm<HR, KS, (MG < 2 ? MG : 2)>(a, frag, row_score, s);
-  if (need <= 4 || MG < 8) return launch_wide_nm<HR, KS, (MG < 4 ? MG : 4)>(a, frag, row_score, s);
-  return launch_wide_nm<HR, KS, (MG < 8 ? MG : 8)>(a, frag, row_score, s);
+  if (need <= 1) return launch_wide_nm<HR, KS, 1>(a, frag, ws, s);
+  if (need <= 2 || MG < 4) return launch_wide_nm<HR, KS, (MG < 2 ? MG : 2)>(a, frag, ws, s);
+  if (need <= 4 || MG < 8) return launch_wide_nm<HR, KS, (MG < 4 ? MG : 4)>(a, frag, ws, s);
+  return launch_wide_nm<HR, KS, (MG < 8 ? MG : 8)>(a, frag, ws, s);
 }
 
 template <typename T, int EPL>
@@ -375,17 +418,17 @@ hipError_t launch_prep_wide(const msa_route_args &a, const float *qhat, u32x4 *f
   return hipGetLastError();
 }
 
-hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, float *row_score, hipStream_t s) {
+hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, const RouteWs &ws, hipStream_t s) {
   switch (a.n_router_heads * 8 + a.router_dim / 32) {
-    case 1 * 8 + 2: return launch_wide_t<1, 2>(a, frag, row_score, s);
-    case 1 * 8 + 4: return launch_wide_t<1, 4>(a, frag, row_score, s);
-    case 2 * 8 + 2: return launch_wide_t<2, 2>(a, frag, row_score, s);
-    case 2 * 8 + 4: return launch_wide_t<2, 4>(a, frag, row_score, s);
-    case 4 * 8 + 2: return launch_wide_t<4, 2>(a, frag, row_score, s);
-    case 4 * 8 + 4: return launch_wide_t<4, 4>(a, frag, row_score, s);
-    case 8 * 8 + 2: return launch_wide_t<8, 2>(a, frag, row_score, s);
-    case 8 * 8 + 4: return launch_wide_t<8, 4>(a, frag, row_score, s);
-    case 16 * 8 + 2: return launch_wide_t<16, 2>(a, frag, row_score, s);
+    case 1 * 8 + 2: return launch_wide_t<1, 2>(a, frag, ws, s);
+    case 1 * 8 + 4: return launch_wide_t<1, 4>(a, frag, ws, s);
+    case 2 * 8 + 2: return launch_wide_t<2, 2>(a, frag, ws, s);
+    case 2 * 8 + 4: return launch_wide_t<2, 4>(a, frag, ws, s);
+    case 4 * 8 + 2: return launch_wide_t<4, 2>(a, frag, ws, s);
+    case 4 * 8 + 4: return launch_wide_t<4, 4>(a, frag, ws, s);
+    case 8 * 8 + 2: return launch_wide_t<8, 2>(a, frag, ws, s);
+    case 8 * 8 + 4: return launch_wide_t<8, 4>(a, frag, ws, s);
+    case 16 * 8 + 2: return launch_wide_t<16, 2>(a, frag, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

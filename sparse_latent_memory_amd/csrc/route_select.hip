@@ -10,22 +10,23 @@
 // are loaded from host memory to the GPU).
 //
 // Kernels, in launch order:
-//  1. block    per 256-document block: per-document max -> doc_scores, block
-//              top-k by a bitonic sort in LDS -> candidates.
-//  2. final    one workgroup per query selects the exact top-k: the k-th
-//              largest block maximum T bounds the global k-th key from below
-//              and only the k blocks whose maximum is >= T can hold winners,
-//              so at most k*k keys are ranked; a radix select over
-//              wave-private histograms covers what that path does not
-//              (k > 64, more than 4096 blocks).  With device-side assembly it
-//              also writes the copy plan.
-// The final survivors (at most one per thread) are ordered by rank counting
-// rather than sorting: a key's rank is the number of keys before it
-// (greater, or equal and at a lower index), found by one pass over the set
-// in LDS (every lane of a wave reads the same word, a broadcast) behind a
-// single barrier, where a bitonic sort of 256 keys takes 36 barrier-separated
-// stages (measured 2 us faster).  The 256-document blocks and the block
-// maxima stay sorted: there the rank pass measured slower than the sort.
+//  0. map      (document path only, before the scan) per 16-row tile of the
+//              bank: the document holding its first row and a bit per row
+//              that starts a document, so the scan can reduce each tile per
+//              document itself.
+//  1. reduce   per block of 256 documents: each document's score ->
+//              doc_scores, and the block's best document key -> blockmax.
+//              Row path: the max over the document's row scores.  Document
+//              path: the max of the scan's part for the tile where the
+//              document starts and its continuation parts in later tiles.
+//  2. final    one workgroup per query selects the exact top-k: T, the k-th
+//              largest block-maximum score, bounds the global k-th key from
+//              below (the k blocks behind those maxima hold k keys >= T), so
+//              only the blocks whose maximum scores >= T can hold winners;
+//              their documents' keys >= T are collected and ordered.  A radix
+//              select over all documents covers what that path does not
+//              (k > 64, more than 4096 blocks, or too many survivors).  With
+//              device-side assembly it also writes the copy plan.
 //  3. gather   (device-side assembly only) copy the selected documents'
 //              pooled K/V rows from mapped pinned host memory into mem_kv.
 // Keys are (order-preserving score bits << 32) | (0xffffffff - doc id), so one
@@ -38,13 +39,10 @@ namespace msa {
 namespace {
 
 constexpr int kWaves = kDocsPerBlock / 64;   // waves per workgroup
-constexpr int kSortCap = kMaxTopK;           // keys the final selection can sort in LDS
-constexpr int kFastTopK = 64;                // k up to this uses the block-maximum bound (<= k*k survivors)
+constexpr int kSortCap = kMaxTopK;           // keys the final selection can order in LDS
+constexpr int kFastTopK = 64;                // k up to this uses the block-maximum bound
 constexpr int kBallotLists = 16;             // block maxima per lane in the ballot threshold (<= 1024 blocks)
 
-// --------------------------------------------------------------------------
-// per-document max, block top-k, and the exact final top-k
-// --------------------------------------------------------------------------
 __device__ void bitonic_desc(uint64_t *key, int n) {  // n a power of two; all threads call
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -76,21 +74,73 @@ __device__ __forceinline__ uint64_t doc_key(float score, int d) {
   return ((uint64_t)score_key(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)d);
 }
 
-// Per 256-document block: per-document max -> doc_scores, and the block's
-// top-cpb keys sorted descending -> cand.  row_score holds n_parts partial
-// token maxima per query and row; the document max runs over all of them.
-__global__ __launch_bounds__(kDocsPerBlock) void doc_block_topk_kernel(
+__device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t n_pool) {
+  return r < 0 ? 0 : (r > n_pool ? n_pool : r);
+}
+
+// Maximum of one key per thread over the workgroup (all threads call; the
+// result is valid in every thread).
+__device__ __forceinline__ uint64_t block_max_key(uint64_t k, uint64_t *red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t y = __shfl_xor(k, o, 64);
+    k = y > k ? y : k;
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();                       // red[] free from a previous use
+  if ((threadIdx.x & 63) == 0) red[wave] = k;
+  __syncthreads();
+  uint64_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = red[w] > m ? red[w] : m;
+  return m;
+}
+
+// --------------------------------------------------------------------------
+// 0. document map (document path)
+// --------------------------------------------------------------------------
+// Thread d owns the tiles whose first row lies in document d (with valid
+// offsets every tile has exactly one such document): it records d and the
+// rows of the tile where a document starts, including the bank's end (row
+// n_pool), which keeps the rows past it out of every document.
+__global__ __launch_bounds__(256) void doc_map_kernel(const int64_t *__restrict__ pool_off,
+                                                      int32_t *__restrict__ tile_doc,
+                                                      uint32_t *__restrict__ tile_bits, int n_docs,
+                                                      int64_t n_pool) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= n_docs) return;
+  const int64_t r0 = clamp_row(pool_off[d], n_pool);
+  const int64_t r1 = max(r0, clamp_row(pool_off[d + 1], n_pool));
+  const int64_t n_tiles = (n_pool + 15) >> 4;
+  for (int64_t t = (r0 + 15) >> 4; t * 16 < r1 && t < n_tiles; ++t) {
+    const int64_t base = t * 16;
+    uint32_t bits = r0 == base ? 1u : 0u;
+    for (int i = 1; i <= 16 && d + i <= n_docs; ++i) {   // a tile holds at most 16 starts
+      const int64_t s = d + i < n_docs ? clamp_row(pool_off[d + i], n_pool) : n_pool;
+      if (s >= base + 16) break;
+      if (s > base) bits |= 1u << (s - base);
+    }
+    tile_doc[t] = d;
+    tile_bits[t] = bits;
+  }
+}
+
+// --------------------------------------------------------------------------
+// 1. per-document scores and block maxima
+// --------------------------------------------------------------------------
+// Row path: per 256-document block and query, the max over the document's
+// row scores (row_score holds n_parts partial token maxima per query and
+// row; the document max runs over all of them).
+__global__ __launch_bounds__(kDocsPerBlock) void doc_rows_kernel(
     const float *__restrict__ row_score, const int64_t *__restrict__ pool_off, float *__restrict__ doc_scores,
-    uint64_t *__restrict__ cand, int n_docs, int64_t n_pool, int cpb, int n_parts) {
-  __shared__ uint64_t key[kDocsPerBlock];
+    uint64_t *__restrict__ blockmax, int n_docs, int64_t n_pool, int n_parts) {
+  __shared__ uint64_t red[kWaves];
   const int b = blockIdx.y, n_blocks = gridDim.x;
-  const int tid = threadIdx.x;
-  const int d = blockIdx.x * kDocsPerBlock + tid;
+  const int d = blockIdx.x * kDocsPerBlock + threadIdx.x;
   uint64_t kk = 0;
   if (d < n_docs) {
-    int64_t r0 = pool_off[d], r1 = pool_off[d + 1];
-    r0 = max((int64_t)0, min(r0, n_pool));
-    r1 = max(r0, min(r1, n_pool));
+    const int64_t r0 = clamp_row(pool_off[d], n_pool);
+    const int64_t r1 = max(r0, clamp_row(pool_off[d + 1], n_pool));
     float best = -INFINITY;
     for (int part = 0; part < n_parts; ++part) {
       const float *rs = row_score + ((int64_t)b * n_parts + part) * n_pool;
@@ -104,22 +154,70 @@ __global__ __launch_bounds__(kDocsPerBlock) void doc_block_topk_kernel(
     doc_scores[(int64_t)b * n_docs + d] = best;
     kk = doc_key(best, d);
   }
-  key[tid] = kk;
-  __syncthreads();
-  bitonic_desc(key, kDocsPerBlock);
-  uint64_t *my = cand + ((int64_t)b * n_blocks + blockIdx.x) * cpb;
-  for (int i = tid; i < cpb; i += blockDim.x) my[i] = key[i];
+  const uint64_t m = block_max_key(kk, red);
+  if (threadIdx.x == 0) blockmax[(int64_t)b * n_blocks + blockIdx.x] = m;
 }
 
-// One workgroup per query: the exact top-k of the n_blocks sorted candidate
-// lists (and, for device-side assembly, the copy plan).  A separate launch
-// rather than a last-block-done tail on the kernel above: the device-scope
-// release every block would need writes back its XCD's L2, and hundreds of
-// those cost far more than one kernel boundary.
+// Document path: per 256-document block and QC queries (the query stride
+// is a multiple of QC), a document's score is the max of the scan's part
+// for the tile where it starts and the continuation parts of the later
+// tiles it covers.
+template <int QC>
+__global__ __launch_bounds__(kDocsPerBlock) void doc_parts_kernel(
+    const float *__restrict__ doc_part, const float *__restrict__ tile_cont, const int64_t *__restrict__ pool_off,
+    float *__restrict__ doc_scores, uint64_t *__restrict__ blockmax, int n_docs, int64_t n_pool, int B,
+    int qstride) {
+  __shared__ uint64_t red[kWaves];
+  const int n_blocks = gridDim.x;
+  const int q0 = blockIdx.y * QC;
+  const int d = blockIdx.x * kDocsPerBlock + threadIdx.x;
+  const bool valid = d < n_docs;
+  float sc[QC];
+#pragma unroll
+  for (int i = 0; i < QC; ++i) sc[i] = -INFINITY;
+  if (valid) {
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(doc_part + (int64_t)d * qstride + q0);
+#pragma unroll
+    for (int v = 0; v < QC / 4; ++v) {
+      const f32x4 x = p[v];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[4 * v + e] = x[e];
+    }
+    const int64_t r0 = clamp_row(pool_off[d], n_pool);
+    const int64_t r1 = max(r0, clamp_row(pool_off[d + 1], n_pool));
+    if (r1 > r0) {
+      for (int64_t t = (r0 >> 4) + 1; t <= ((r1 - 1) >> 4); ++t) {   // tiles the document continues into
+        const f32x4 *c = reinterpret_cast<const f32x4 *>(tile_cont + t * qstride + q0);
+#pragma unroll
+        for (int v = 0; v < QC / 4; ++v) {
+          const f32x4 x = c[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[4 * v + e] = fmaxf(sc[4 * v + e], x[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < QC; ++i) {
+    const int b = q0 + i;
+    if (b >= B) break;                   // (uniform)
+    if (valid) doc_scores[(int64_t)b * n_docs + d] = sc[i];
+    const uint64_t m = block_max_key(valid ? doc_key(sc[i], d) : 0, red);
+    if (threadIdx.x == 0) blockmax[(int64_t)b * n_blocks + blockIdx.x] = m;
+  }
+}
+
+// --------------------------------------------------------------------------
+// 2. exact top-k per query
+// --------------------------------------------------------------------------
+// A separate launch rather than a last-block-done tail on the kernel above:
+// the device-scope release every block would need writes back its XCD's L2,
+// and hundreds of those cost far more than one kernel boundary.
 __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
-    const uint64_t *__restrict__ cand, const int64_t *__restrict__ pool_off, int32_t *__restrict__ topk_idx,
-    float *__restrict__ topk_score, GatherPlan *__restrict__ plan, int32_t *__restrict__ mem_len, int mem_cap,
-    int append, int n_blocks, int64_t n_pool, int cpb, int k) {
+    const uint64_t *__restrict__ blockmax, const float *__restrict__ doc_scores,
+    const int64_t *__restrict__ pool_off, int32_t *__restrict__ topk_idx, float *__restrict__ topk_score,
+    GatherPlan *__restrict__ plan, int32_t *__restrict__ mem_len, int mem_cap, int append, int n_blocks,
+    int n_docs, int64_t n_pool, int k) {
   __shared__ uint64_t sel[kSortCap];
   __shared__ uint32_t hist[kWaves][256];
   __shared__ int top_blk[kFastTopK];
@@ -130,20 +228,16 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
   __shared__ uint64_t s_prefix, s_mask;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6;
+  const uint64_t *bm = blockmax + (int64_t)b * n_blocks;
+  const float *ds = doc_scores + (int64_t)b * n_docs;
 
-  const uint64_t *c = cand + (int64_t)b * n_blocks * cpb;
-  const int n_cand = n_blocks * cpb;
   bool sorted = false;
-  if (k <= cpb && k <= kFastTopK && n_blocks <= kSortCap) {
-    // Every list is sorted, so its first key is its block's maximum.  With T
-    // the k-th largest block maximum, at least k keys are >= T, so every
-    // global top-k key is >= T and sits in one of the k blocks whose maximum
-    // is >= T, inside that block's top-k list: only those k lists are read.
+  if (k <= kFastTopK && n_blocks <= kSortCap) {
     if (n_blocks <= 64 * kBallotLists) {
-      // Wave 0 finds the score half T of that bound bit by bit: each lane
+      // Wave 0 finds the score half T of the bound bit by bit: each lane
       // holds up to kBallotLists block maxima, and the count of maxima
       // scoring >= a candidate is a sum of ballot popcounts (no barrier, no
-      // sort).  The lists whose maximum scores >= T - k of them, more only
+      // sort).  The blocks whose maximum scores >= T - k of them, more only
       // where scores tie - hold every winner, all with keys >= T << 32.
       if (wave == 0) {
         const int lane = tid & 63;
@@ -151,7 +245,7 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
 #pragma unroll
         for (int m = 0; m < kBallotLists; ++m) {
           const int i = lane + 64 * m;
-          sk[m] = i < n_blocks ? (uint32_t)(c[(int64_t)i * cpb] >> 32) : 0u;
+          sk[m] = i < n_blocks ? (uint32_t)(bm[i] >> 32) : 0u;
         }
         uint32_t T = 0;
         for (int bit = 31; bit >= 0; --bit) {
@@ -181,7 +275,7 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
     } else {
       int nb2 = 1;
       while (nb2 < n_blocks) nb2 <<= 1;
-      for (int i = tid; i < nb2; i += blockDim.x) sel[i] = i < n_blocks ? c[(int64_t)i * cpb] : 0;
+      for (int i = tid; i < nb2; i += blockDim.x) sel[i] = i < n_blocks ? bm[i] : 0;
       __syncthreads();
       bitonic_desc(sel, nb2);
       const int nb = min(k, n_blocks);
@@ -196,11 +290,27 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
     const int nb = s_nb;
     const uint64_t thr = s_thr;
     if (nb <= kFastTopK) {
-      for (int i = tid; i < nb * cpb; i += blockDim.x) {
-        const uint64_t x = c[(int64_t)top_blk[i / cpb] * cpb + i % cpb];
-        if (x >= thr) {
-          const int pos = atomicAdd(&s_count, 1);
-          if (pos < kSortCap) sel[pos] = x;
+      // the documents of the selected blocks whose keys reach the bound:
+      // thread t takes position t of every block, eight blocks' loads in
+      // flight before any is used (blockDim == kDocsPerBlock)
+      for (int j0 = 0; j0 < nb; j0 += 8) {
+        float v[8];
+        int dd[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int blk = j0 + u < nb ? min(max(top_blk[j0 + u], 0), n_blocks - 1) : 0;
+          dd[u] = j0 + u < nb ? blk * kDocsPerBlock + tid : n_docs;
+          v[u] = dd[u] < n_docs ? ds[dd[u]] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (dd[u] < n_docs) {
+            const uint64_t x = doc_key(v[u], dd[u]);
+            if (x >= thr) {
+              const int pos = atomicAdd(&s_count, 1);
+              if (pos < kSortCap) sel[pos] = x;
+            }
+          }
         }
       }
       __syncthreads();
@@ -208,7 +318,8 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
     }
   }
   if (!sorted) {
-    // radix select of the k-th largest key, 8 bits per pass, wave-private histograms
+    // radix select of the k-th largest document key, 8 bits per pass,
+    // wave-private histograms
     if (tid == 0) { s_prefix = 0; s_mask = 0; s_need = k; s_count = 0; }
     __syncthreads();
     for (int pass = 0; pass < 8; ++pass) {
@@ -216,8 +327,8 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
       for (int i = tid; i < kWaves * 256; i += blockDim.x) (&hist[0][0])[i] = 0;
       __syncthreads();
       const uint64_t prefix = s_prefix, mask = s_mask;
-      for (int i = tid; i < n_cand; i += blockDim.x) {
-        const uint64_t x = c[i];
+      for (int d = tid; d < n_docs; d += blockDim.x) {
+        const uint64_t x = doc_key(ds[d], d);
         if ((x & mask) == prefix) atomicAdd(&hist[wave][(x >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -242,8 +353,8 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
       __syncthreads();
     }
     const uint64_t thr = s_prefix;   // the k-th largest key exactly (keys are unique)
-    for (int i = tid; i < n_cand; i += blockDim.x) {
-      const uint64_t x = c[i];
+    for (int d = tid; d < n_docs; d += blockDim.x) {
+      const uint64_t x = doc_key(ds[d], d);
       if (x >= thr) {
         const int pos = atomicAdd(&s_count, 1);
         if (pos < kSortCap) sel[pos] = x;
@@ -251,10 +362,13 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
     }
     __syncthreads();
   }
+  // Order the survivors.  At most one per thread: rank counting (a key's
+  // rank is the number of keys before it, greater or equal at a lower index,
+  // found by one broadcast pass over LDS behind a single barrier, where a
+  // bitonic sort of 256 keys takes 36 barrier-separated stages); more: sort.
   const int n_sel = min(s_count, kSortCap);
   uint64_t *top = sel;                   // the k winners in order
   if (k <= kFastTopK && n_sel <= (int)blockDim.x && n_sel >= k) {
-    // one survivor per thread (at least k of them: every top-k key survives)
     if (tid < n_sel) {
       const uint64_t x = sel[tid];
       const int r = rank_of(sel, n_sel, x, tid);
@@ -279,10 +393,9 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
   __shared__ int32_t prow[kMaxTopK], pdst[kMaxTopK];
   __syncthreads();                       // top[] is reused below
   for (int r = tid; r < k; r += blockDim.x) {   // every rank's offsets loaded in parallel
-    const int dd = (int)(0xffffffffu - (uint32_t)(top[r] & 0xffffffffu));
-    int64_t r0 = pool_off[dd], r1 = pool_off[dd + 1];
-    r0 = max((int64_t)0, min(r0, n_pool));
-    r1 = max(r0, min(r1, n_pool));
+    const int dd = min(max((int)(0xffffffffu - (uint32_t)(top[r] & 0xffffffffu)), 0), n_docs - 1);
+    const int64_t r0 = clamp_row(pool_off[dd], n_pool);
+    const int64_t r1 = max(r0, clamp_row(pool_off[dd + 1], n_pool));
     top[r] = (uint64_t)r0;
     prow[r] = (int32_t)min(r1 - r0, (int64_t)mem_cap + 1);
   }
@@ -310,7 +423,7 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
 }
 
 // --------------------------------------------------------------------------
-// device-side assembly: one workgroup per (rank, query), reading the
+// 3. device-side assembly: one workgroup per (rank, query), reading the
 //    selected rows over the host link from mapped pinned memory
 // --------------------------------------------------------------------------
 constexpr int kGatherInflight = 4;
@@ -338,15 +451,35 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
 
 }  // namespace
 
+hipError_t launch_doc_map(const msa_route_args &a, const RouteWs &ws, hipStream_t s) {
+  hipLaunchKernelGGL(doc_map_kernel, dim3((a.n_docs + 255) / 256), dim3(256), 0, s, a.doc_pool_off, ws.tile_doc,
+                     ws.tile_bits, a.n_docs, a.n_pool);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const msa_route_args &a, const RouteWs &ws, const void *host_kv_dev, hipStream_t s) {
   const bool device_gather = host_kv_dev != nullptr;
-  hipLaunchKernelGGL(doc_block_topk_kernel, dim3(ws.n_blocks, a.batch), dim3(kDocsPerBlock), 0, s, ws.row_score,
-                     a.doc_pool_off, a.doc_scores, ws.cand, a.n_docs, a.n_pool, ws.cand_per_block, ws.n_parts);
+  if (ws.qstride > 0) {
+    // query chunk: 16 on the wide scan's stride (a multiple of 16), else the stride (4 or 8)
+    const int qc = ws.qstride % 16 == 0 ? 16 : ws.qstride;
+    const dim3 grid(ws.n_blocks, (a.batch + qc - 1) / qc);
+    if (qc == 16)
+      hipLaunchKernelGGL(doc_parts_kernel<16>, grid, dim3(kDocsPerBlock), 0, s, ws.doc_part, ws.tile_cont,
+                         a.doc_pool_off, a.doc_scores, ws.blockmax, a.n_docs, a.n_pool, a.batch, ws.qstride);
+    else if (qc == 8)
+      hipLaunchKernelGGL(doc_parts_kernel<8>, grid, dim3(kDocsPerBlock), 0, s, ws.doc_part, ws.tile_cont,
+                         a.doc_pool_off, a.doc_scores, ws.blockmax, a.n_docs, a.n_pool, a.batch, ws.qstride);
+    else
+      hipLaunchKernelGGL(doc_parts_kernel<4>, grid, dim3(kDocsPerBlock), 0, s, ws.doc_part, ws.tile_cont,
+                         a.doc_pool_off, a.doc_scores, ws.blockmax, a.n_docs, a.n_pool, a.batch, ws.qstride);
+  } else
+    hipLaunchKernelGGL(doc_rows_kernel, dim3(ws.n_blocks, a.batch), dim3(kDocsPerBlock), 0, s, ws.row_score,
+                       a.doc_pool_off, a.doc_scores, ws.blockmax, a.n_docs, a.n_pool, ws.n_parts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3(a.batch), dim3(kDocsPerBlock), 0, s, ws.cand, a.doc_pool_off,
-                     a.topk_idx, a.topk_score, device_gather ? ws.plan : nullptr, a.mem_len, a.mem_cap, a.append,
-                     ws.n_blocks, a.n_pool, ws.cand_per_block, a.top_k);
+  hipLaunchKernelGGL(topk_final_kernel, dim3(a.batch), dim3(kDocsPerBlock), 0, s, ws.blockmax, a.doc_scores,
+                     a.doc_pool_off, a.topk_idx, a.topk_score, device_gather ? ws.plan : nullptr, a.mem_len,
+                     a.mem_cap, a.append, ws.n_blocks, a.n_docs, a.n_pool, a.top_k);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (device_gather) {
     const size_t elt = a.kv_dtype == MSA_BF16 ? 2 : 4;

@@ -65,7 +65,10 @@ def test_ctypes_struct_layout_matches_c(tmp_path):
 
 def test_workspace_size_functions():
     lib = _lib.load()
-    assert lib.msa_route_workspace_bytes(1, 1, 1, 8, 128, 195313, 1562504, 16) >= 4 * 1562504
+    # one token per query: per-document parts (a stride of 4 queries) and per-tile continuations
+    assert lib.msa_route_workspace_bytes(1, 1, 1, 8, 128, 195313, 1562504, 16) >= 16 * 195313 + 16 * 97657
+    # several tokens: one score per bank row and query
+    assert lib.msa_route_workspace_bytes(1, 1, 2, 8, 128, 195313, 1562504, 16) >= 4 * 1562504
     assert lib.msa_route_workspace_bytes(1, 0, 1, 8, 128, 10, 10, 1) == 0          # batch 0
     assert lib.msa_route_workspace_bytes(7, 1, 1, 8, 128, 10, 10, 1) == 0          # bad dtype
     assert lib.msa_route_workspace_bytes(1, 1, 1, 8, 128, 10, 9, 1) == 0           # n_pool < n_docs

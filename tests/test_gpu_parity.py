@@ -198,6 +198,32 @@ def test_pool_tiled_router_bank_at_row_offsets():
     assert torch.equal(kt2.view(torch.int16), whole.view(torch.int16))
 
 
+@pytest.mark.parametrize("hr,dr,host", [(2, 64, False), (1, 128, True), (16, 64, False)])
+def test_pool_tiled_router_bank_shapes_and_pinned_output(hr, dr, host):
+    """The tiled writer at other router shapes (2, 1 and 16 heads), and into
+    pinned host memory: always the row-major output, permuted."""
+    g = torch.Generator().manual_seed(40 + hr * dr)
+    lens = np.concatenate([[1, 63, 64, 65], torch.randint(1, 400, (30,), generator=g).numpy()])
+    n = int(lens.sum())
+    P = 64
+    pool_off = synth.row_offsets(lens, P)
+    n_pool = int(pool_off[-1])
+    k = _randn(g, n, 2, 64, dtype=torch.bfloat16).to(DEV)
+    v = _randn(g, n, 2, 64, dtype=torch.bfloat16).to(DEV)
+    kr = _randn(g, n, hr, dr, dtype=torch.bfloat16).to(DEV)
+    _say(f"pool: tiled router bank Hr={hr} dr={dr}, {n_pool} rows at row 3, {'pinned host' if host else 'device'}")
+    tok = _dev(synth.token_offsets(lens))
+    _, kr_r = msa.pool_encode(k, v, kr, tok, _dev(pool_off), P, THETA, n_pool)
+    shape = (msa.bank_rows(3 + n_pool, "tiled"), hr, dr)
+    kt = torch.zeros(shape, dtype=torch.bfloat16, pin_memory=True) if host else \
+        torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
+    msa.pool_encode(k, v, kr, tok, _dev(pool_off), P, THETA, n_pool, kr_pooled=kt, kr_layout="tiled", kr_row_base=3)
+    torch.cuda.synchronize()
+    rows = synth.untile_router_bank(kt.to(DEV), kt.shape[0])
+    assert torch.equal(rows[3:3 + n_pool].view(torch.int16), kr_r.view(torch.int16))
+    assert not rows[:3].view(torch.int16).any() and not rows[3 + n_pool:].view(torch.int16).any()
+
+
 # ==========================================================================
 # stage 2: routing
 # ==========================================================================
@@ -316,6 +342,44 @@ def test_route_ties_go_to_lower_document_id(dtype):
     assert idx[:5].tolist() == twins
     assert len(set(np64(sc)[0, :5].tolist())) == 1
     check_topk(idx[None], oracle.doc_scores(np64(qr), np64(kr), off), 8, "ties")
+
+
+@pytest.mark.parametrize("b", [9, 17, 64])
+@pytest.mark.parametrize("k", [1, 16, 64, 65, 300])
+def test_route_document_path(b, k):
+    """One-token batches (the scan reduces each tile per document itself):
+    documents of 1 to 70 rows (runs within a tile, documents over many
+    tiles), every selection branch (k up to 64 uses the block bound; 65 and
+    all documents the radix select), checked against the oracle and, tiled
+    with NaN in its padding rows, against the row-major bank bit for bit."""
+    g = torch.Generator().manual_seed(3000 + b * 11 + k)
+    rows = np.where(torch.rand(300, generator=g).numpy() < 0.2,
+                    torch.randint(17, 71, (300,), generator=g).numpy(),
+                    torch.randint(1, 5, (300,), generator=g).numpy())
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    kr = _randn(g, int(off[-1]), 8, 128, dtype=torch.bfloat16).to(DEV)
+    qr = _randn(g, b, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+    _say(f"route: document path B={b} k={k}, 300 docs, {off[-1]} rows")
+    _route_check(kr, off, qr, k, f"docs B{b} k{k}")
+    _route_both_layouts(qr, kr, off, k, f"docs tiled B{b} k{k}")
+
+
+def test_route_document_path_ties_and_whole_tiles():
+    """Exact ties between documents on the document path, and a bank whose
+    documents are 16-row multiples (every tile starts a document or
+    continues one whole)."""
+    g = torch.Generator().manual_seed(8)
+    rows = np.array([16, 32, 16, 48, 16] * 20)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    kr = _randn(g, int(off[-1]), 8, 128, dtype=torch.bfloat16).to(DEV)
+    hot = _randn(g, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+    twins = [3, 4, 41, 77, 99]
+    for d in twins:
+        kr[int(off[d + 1]) - 1] = hot[0]         # the last row of each twin
+    qr = hot[None].repeat(12, 1, 1, 1).clone()
+    _say("route: document path, ties, 16-row documents, B=12")
+    idx, _ = _route_check(kr, off, qr, 8, "docs ties")
+    assert all(idx[b, :5].tolist() == twins for b in range(12))
 
 
 def test_route_all_documents_and_degenerate_rows():
