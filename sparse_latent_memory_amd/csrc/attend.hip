@@ -58,6 +58,12 @@ constexpr int kAMaxSplit = 4096;
 #ifndef MSA_ATT_ORDER       // work item order: 0 split fastest, 1 KV head fastest
 #define MSA_ATT_ORDER 1
 #endif
+#ifndef MSA_ATT_PREROT      // 1: rotate local keys once when several query tiles read them
+#define MSA_ATT_PREROT 1
+#endif
+#ifndef MSA_ATT_MERGE_WAVE  // 1: merge with one wave per output row when there are at most 64 splits
+#define MSA_ATT_MERGE_WAVE 1
+#endif
 #ifndef MSA_ATT_ROTATE      // 1: rotate each query's split order by its index
 #define MSA_ATT_ROTATE 1
 #endif
@@ -90,7 +96,9 @@ __device__ __forceinline__ uint32_t bf16_at(const u32x2 &v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <int D>
+// PREROT: the local keys come already rotated to their positions (o + i),
+// from rope_local_kernel; the kernel then rotates nothing but the query.
+template <int D, bool PREROT>
 __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
     const uint16_t *__restrict__ local_k, const uint16_t *__restrict__ local_v,
@@ -111,25 +119,43 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
   __shared__ __align__(16) uint16_t vt_all[kAWaves][D * VTS];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  int64_t item = (int64_t)blockIdx.x * kAWaves + wave;
-  const bool live = item < (int64_t)B * Hkv * n_mt * n_split;
-  if (!live) item = 0;                                     // decoded but never written
+  int g, split_i, mt, b;
+  bool live;
+  if (n_mt > 1) {
+    // Several query tiles per KV head read the same keys: workgroup w serves
+    // KV head w % Hkv only.  Workgroups go round-robin over the 8 XCDs, so an
+    // XCD's L2 holds the keys of one head (Hkv = 8), or of a few, instead of
+    // all of them.  Its waves take consecutive (query, tile, split) items of
+    // that head.
+    g = (int)(blockIdx.x % Hkv);
+    int64_t r = (int64_t)(blockIdx.x / Hkv) * kAWaves + wave;
+    live = r < (int64_t)B * n_mt * n_split;
+    if (!live) r = 0;                                      // decoded but never written
+    split_i = (int)(r % n_split);
+    r /= n_split;
+    mt = (int)(r % n_mt);
+    b = (int)(r / n_mt);
+  } else {
+    int64_t item = (int64_t)blockIdx.x * kAWaves + wave;
+    live = item < (int64_t)B * Hkv * n_mt * n_split;
+    if (!live) item = 0;                                   // decoded but never written
 #if MSA_ATT_ORDER == 1
-  // KV head fastest: the Hkv waves of one key range read whole K/V rows together
-  const int g = (int)(item % Hkv);
-  item /= Hkv;
-  const int split_i = (int)(item % n_split);
-  item /= n_split;
-  const int mt = (int)(item % n_mt);
-  const int b = (int)(item / n_mt);
+    // KV head fastest: the Hkv waves of one key range read whole K/V rows together
+    g = (int)(item % Hkv);
+    item /= Hkv;
+    split_i = (int)(item % n_split);
+    item /= n_split;
+    mt = (int)(item % n_mt);
+    b = (int)(item / n_mt);
 #else
-  const int split_i = (int)(item % n_split);
-  item /= n_split;
-  const int mt = (int)(item % n_mt);
-  item /= n_mt;
-  const int g = (int)(item % Hkv);
-  const int b = (int)(item / Hkv);
+    split_i = (int)(item % n_split);
+    item /= n_split;
+    mt = (int)(item % n_mt);
+    item /= n_mt;
+    g = (int)(item % Hkv);
+    b = (int)(item / Hkv);
 #endif
+  }
 #if MSA_ATT_ROTATE
   const int split = (int)((split_i + 5LL * b) % n_split);  // queries walk their key ranges out of step
 #else
@@ -149,6 +175,7 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
   const bool row_ok = R < n_rows;
   const int t_row = row_ok ? R / G : 0;
   const int i_row = T - Tq + t_row;                        // local index of the row's token
+  const int i_first = T - Tq + (mt * 16) / G;              // ... of the tile's first token
   // keys the tile can see: the memory, then local tokens up to its last token
   const int t_last = min(Tq - 1, (mt * 16 + 15) / G);
   const int key_end = M + max(0, min(T, T - Tq + t_last + 1));
@@ -220,27 +247,33 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
       }
     }
 
-    const int64_t mem_row = 2LL * Hkv * D, loc_row = (int64_t)Hkv * D;
-    auto kaddr = [&](int k) -> const uint16_t * {
-      return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mem_row + (int64_t)g * D
-                   : local_k + ((int64_t)b * local_cap + (k - M)) * loc_row + (int64_t)g * D;
-    };
-    auto vaddr = [&](int k) -> const uint16_t * {
-      return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mem_row + loc_row + (int64_t)g * D
-                   : local_v + ((int64_t)b * local_cap + (k - M)) * loc_row + (int64_t)g * D;
+    // Key k lives in memory row k (k < M) or local row k - M; its K and V
+    // are selected branch-free: element offset base + k * stride in the
+    // array of its kind (one 32 x 32 -> 64-bit multiply-add per key).
+    const uint32_t mrow = 2u * Hkv * D, lrow = (uint32_t)Hkv * D;
+    const int64_t mem_base = (int64_t)b * mem_cap * mrow + (int64_t)g * D;
+    const int64_t loc_base = ((int64_t)b * local_cap - M) * lrow + (int64_t)g * D;   // + k * lrow for k >= M
+    auto key_ptrs = [&](int k, const uint16_t *&kp, const uint16_t *&vp) {
+      const bool mem = k < M;
+      const int64_t off = (mem ? mem_base : loc_base) + (int64_t)((uint64_t)(uint32_t)k * (mem ? mrow : lrow));
+      kp = (mem ? mem_kv : local_k) + off;
+      vp = (mem ? mem_kv + lrow : local_v) + off;
     };
     // loads of the 16-key group at kb (keys past k_end read key k_end - 1;
     // their scores are masked)
     const int kq = lane & 3, db = lane >> 2;                // V staging: keys 4kq.., dims db*DB..
     auto load = [&](int kb, u32x4 *kf, VVec *vv) {
-      const int kk = min(kb + col, k_end - 1);
-      const uint16_t *ks = kaddr(kk) + 8 * grp;
+      const bool inside = kb + 15 < k_end;                  // (uniform) no clamping needed
+      const uint16_t *kp, *vp;
+      key_ptrs(inside ? kb + col : min(kb + col, k_end - 1), kp, vp);
+      kp += 8 * grp;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[s] = ld16(ks + 32 * s);
+      for (int s = 0; s < KS; ++s) kf[s] = ld16(kp + 32 * s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint16_t *vs = vaddr(min(kb + 4 * kq + i, k_end - 1)) + db * DB;
-        vv[i] = *reinterpret_cast<const VVec *>(vs);
+        const int kv = kb + 4 * kq + i;
+        key_ptrs(inside ? kv : min(kv, k_end - 1), kp, vp);
+        vv[i] = *reinterpret_cast<const VVec *>(vp + db * DB);
       }
     };
 
@@ -284,7 +317,7 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
     // one 16-key group: rotation, S^T = K Q^T, online softmax, V transposed
     // through LDS, O += P V
     auto group = [&](int gi, int kb, u32x4 *kf, const VVec *vv) {
-      if (kb + 15 >= M) rotate(gi, kb, kf);
+      if (!PREROT && kb + 15 >= M) rotate(gi, kb, kf);
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -299,12 +332,16 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
         w.y = bf16_at(vv[2], e) | (bf16_at(vv[3], e) << 16);
         *reinterpret_cast<u32x2 *>(vt + (db * DB + e) * VTS + 4 * kq) = w;
       }
-      // mask: row must exist, key in range, local keys up to the row's token
+      // mask: row must exist, key in range, local keys up to the row's token;
+      // not needed when every key of the group is in range and visible to
+      // the tile's first token (rows that do not exist are never stored)
+      if (!(kb + 15 < k_end && kb + 15 - M <= i_first)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * grp + r;
-        const bool ok = row_ok && key < k_end && (key < M || key - M <= i_row);
-        sc[r] = ok ? sc[r] : -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 4 * grp + r;
+          const bool ok = row_ok && key < k_end && (key < M || key - M <= i_row);
+          sc[r] = ok ? sc[r] : -INFINITY;
+        }
       }
       float mt_ = amax4(sc);
       mt_ = fmaxf(mt_, __shfl_xor(mt_, 16, 64));
@@ -323,15 +360,20 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       l_run = l_run * corr + psum;
-      m_run = m_new;
-      // rows 4 grp + r of the accumulators take the factor of their row
-      float cr[4];
+      // rows 4 grp + r of the accumulators take the factor of their row,
+      // which is exactly 1 unless the row's running max rose
+      if (__any(m_new > m_run)) {
+        float cr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r, 64);
+        for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * grp + r, 64);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][r] *= cr[r];
+      }
+      m_run = m_new;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nt][r] *= cr[r];
         const u32x2 vb = *reinterpret_cast<const u32x2 *>(vt + (16 * nt + col) * VTS + 4 * grp);
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, vb), acc[nt], 0, 0, 0);
       }
@@ -341,7 +383,7 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
     VVec vva[4], vvb[4];
     load(k_begin, kfa, vva);
     for (int ks0 = k_begin; ks0 < k_end; ks0 += 64) {
-      if (ks0 + 63 >= M) block_phasors(ks0);
+      if (!PREROT && ks0 + 63 >= M) block_phasors(ks0);
       // four groups, buffers alternating; the last one loads the next block's first
       load(ks0 + 16, kfb, vvb);
       group(0, ks0, kfa, vva);
@@ -368,6 +410,44 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
       for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[nt][r];
     }
   }
+}
+
+// Local keys rotated once to their positions o + i (i < local_len), for
+// launches in which several query tiles per KV head read every key: thread
+// per (query, token, KV head, 8 pairs), the phasor of each pair evaluated
+// exactly (angle reduced in fp64).
+template <int D>
+__global__ __launch_bounds__(256) void rope_local_kernel(const uint16_t *__restrict__ local_k,
+                                                         const int32_t *__restrict__ local_len,
+                                                         const int32_t *__restrict__ pos_offset,
+                                                         uint16_t *__restrict__ rot_k, int B, int Hkv, int local_cap,
+                                                         double log2_theta) {
+  constexpr int HALF = D / 2, NC = HALF / 8;              // 8-pair chunks per head
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)B * local_cap * Hkv * NC;
+  if (id >= n) return;
+  const int c = (int)(id % NC);
+  const int64_t row = id / NC;                             // (b * local_cap + i) * Hkv + g
+  const int64_t bi = row / Hkv;
+  const int b = (int)(bi / local_cap), i = (int)(bi % local_cap);
+  const int T = max(0, min(local_len[b], local_cap));
+  if (i >= T) return;                                      // never read
+  const double pos = (double)pos_offset[b] + (double)i;
+  const uint16_t *src = local_k + row * D + 8 * c;
+  float a[8], z[8], r1[8], r2[8];
+  Elt<uint16_t>::unpack(ld16(src), a);
+  Elt<uint16_t>::unpack(ld16(src + HALF), z);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = 8 * c + e;
+    float cs, sn;
+    rope_phasor(pos, exp2(-(2.0 * j / D) * log2_theta), &cs, &sn);
+    r1[e] = a[e] * cs - z[e] * sn;
+    r2[e] = z[e] * cs + a[e] * sn;
+  }
+  uint16_t *dst = rot_k + row * D + 8 * c;
+  st16(dst, Elt<uint16_t>::pack(r1));
+  st16(dst + HALF, Elt<uint16_t>::pack(r2));
 }
 
 // Combine the splits of one output row (b, t, h).  Wave 0 forms the
@@ -444,6 +524,64 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const float *__restri
   if (lse && tid == 0) lse[bth] = s_l > 0.f ? (s_m + log2f(s_l)) * 0.69314718055994531f : -INFINITY;
 }
 
+// The same combination with one wave per output row and kAWaves rows per
+// workgroup, for at most 64 splits: lane s holds split s's weight, and the
+// lanes (v, gq) = (lane % NV, lane / NV) own float4 v of the row over splits
+// gq, gq + 64/NV, ...; a butterfly over gq completes the sum.
+template <int D>
+__global__ __launch_bounds__(kAWaves * 64) void attend_merge_wave_kernel(
+    const float *__restrict__ part_acc, const float *__restrict__ part_ml, uint16_t *__restrict__ out,
+    float *__restrict__ lse, int64_t n_out, int Tq, int Hq, int Hkv, int n_mt, int n_split, int rps) {
+  constexpr int NV = D / 4, SG = 64 / NV;
+  const int lane = threadIdx.x & 63;
+  const int64_t bth = (int64_t)blockIdx.x * kAWaves + (threadIdx.x >> 6);  // (b * Tq + t) * Hq + h
+  if (bth >= n_out) return;                                // no barrier in this kernel
+  const int h = (int)(bth % Hq);
+  const int t = (int)((bth / Hq) % Tq);
+  const int b = (int)(bth / ((int64_t)Hq * Tq));
+  const int G = Hq / Hkv, g = h / G;
+  const int R = t * G + (h % G);
+  const int mt = R / 16, row = R % 16;
+  const int64_t base = ((((int64_t)b * Hkv + g) * n_mt + mt) * n_split) * rps + row;   // split s: base + s * rps
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < n_split) {
+    const float2 ml = *reinterpret_cast<const float2 *>(part_ml + 2 * (base + (int64_t)lane * rps));
+    ms = ml.x;
+    ls = ml.y;
+  }
+  const float m = wave_max(ms);
+  const float ws = ms == -INFINITY ? 0.f : exp2f(ms - m);
+  const float l = wave_sum(ws * ls);
+  const int v = lane % NV, gq = lane / NV;
+  float4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += 4 * SG) {
+    float4 x[4];
+    float w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sp = s0 + u * SG + gq;
+      w[u] = __shfl(ws, sp & 63, 64);
+      x[u] = sp < n_split ? reinterpret_cast<const float4 *>(part_acc + (base + (int64_t)sp * rps) * D)[v]
+                          : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a.x += w[u] * x[u].x; a.y += w[u] * x[u].y; a.z += w[u] * x[u].z; a.w += w[u] * x[u].w;
+    }
+  }
+#pragma unroll
+  for (int o = NV; o < 64; o <<= 1) {
+    a.x += __shfl_xor(a.x, o, 64); a.y += __shfl_xor(a.y, o, 64);
+    a.z += __shfl_xor(a.z, o, 64); a.w += __shfl_xor(a.w, o, 64);
+  }
+  if (gq == 0) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    *reinterpret_cast<uint2 *>(out + bth * D + 4 * v) =
+        make_uint2(pack_bf16x2(a.x * inv, a.y * inv), pack_bf16x2(a.z * inv, a.w * inv));
+  }
+  if (lse && lane == 0) lse[bth] = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
 }  // namespace
 
 // Keys per split: enough work items (waves) to give every CU about 16, in
@@ -470,46 +608,67 @@ void attend_plan(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32
 }
 
 size_t attend_ws_layout(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t d, int32_t mem_cap,
-                        int32_t local_cap, void *base, float **part_acc, float **part_ml) {
+                        int32_t local_cap, void *base, AttendWs *ws) {
   AttendPlan p;
   attend_plan(batch, q_tokens, hq, hkv, mem_cap, local_cap, &p);
   const size_t rows = (size_t)batch * hkv * p.n_mt * p.n_split * p.rps;
   const size_t o_ml = (sizeof(float) * rows * d + 255) & ~(size_t)255;
-  const size_t end = (o_ml + sizeof(float) * 2 * rows + 255) & ~(size_t)255;
+  const size_t o_rk = (o_ml + sizeof(float) * 2 * rows + 255) & ~(size_t)255;
+  // several query tiles per KV head read every local key: rotate them once
+  const bool prerot = p.n_mt > 1;
+  const size_t end = prerot ? (o_rk + sizeof(uint16_t) * (size_t)batch * local_cap * hkv * d + 255) & ~(size_t)255
+                            : o_rk;
   if (base) {
-    *part_acc = reinterpret_cast<float *>(base);
-    *part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(base) + o_ml);
+    ws->part_acc = reinterpret_cast<float *>(base);
+    ws->part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(base) + o_ml);
+    ws->rot_k = prerot ? reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(base) + o_rk) : nullptr;
   }
   return end;
 }
 
-template <int D>
-static hipError_t launch_attend_t(const msa_attend_args &a, float *part_acc, float *part_ml, hipStream_t s) {
+template <int D, bool PREROT>
+static hipError_t launch_attend_t(const msa_attend_args &a, const AttendWs &ws, hipStream_t s) {
   AttendPlan p;
   attend_plan(a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap, a.local_cap, &p);
   const float scale = a.softmax_scale > 0.f ? a.softmax_scale : 1.0f / sqrtf((float)D);
-  const int64_t items = (int64_t)a.batch * a.n_kv_heads * p.n_mt * p.n_split;
-  const int64_t grid = (items + kAWaves - 1) / kAWaves;
+  // one KV head per workgroup when several tiles share its keys (see the kernel)
+  const int64_t per_head = (int64_t)a.batch * p.n_mt * p.n_split;
+  const int64_t grid = p.n_mt > 1 ? (int64_t)a.n_kv_heads * ((per_head + kAWaves - 1) / kAWaves)
+                                  : (per_head * a.n_kv_heads + kAWaves - 1) / kAWaves;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
-  hipExtLaunchKernelGGL((attend_kernel<D>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
+  const uint16_t *lk = reinterpret_cast<const uint16_t *>(a.local_k);
+  if (PREROT && lk) {
+    const int64_t n = (int64_t)a.batch * a.local_cap * a.n_kv_heads * (D / 16);
+    hipLaunchKernelGGL((rope_local_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, lk, a.local_len,
+                       a.pos_offset, ws.rot_k, a.batch, a.n_kv_heads, a.local_cap, log2(a.rope_theta));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    lk = ws.rot_k;
+  }
+  hipExtLaunchKernelGGL((attend_kernel<D, PREROT>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
                         prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
                         reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
-                        a.mem_len, reinterpret_cast<const uint16_t *>(a.local_k),
-                        reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset, part_acc,
-                        part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap, a.local_cap, p.n_mt,
-                        p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
+                        a.mem_len, lk, reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset,
+                        ws.part_acc, ws.part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap,
+                        a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = (int64_t)a.batch * a.q_tokens * a.n_q_heads;
-  hipLaunchKernelGGL((attend_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, s, part_acc, part_ml,
-                     reinterpret_cast<uint16_t *>(a.out), a.lse, a.q_tokens, a.n_q_heads, a.n_kv_heads, p.n_mt,
-                     p.n_split, p.rps);
+  if (MSA_ATT_MERGE_WAVE && p.n_split <= 64)
+    hipLaunchKernelGGL((attend_merge_wave_kernel<D>), dim3((unsigned)((rows + kAWaves - 1) / kAWaves)),
+                       dim3(kAWaves * 64), 0, s, ws.part_acc, ws.part_ml, reinterpret_cast<uint16_t *>(a.out), a.lse,
+                       rows, a.q_tokens, a.n_q_heads, a.n_kv_heads, p.n_mt, p.n_split, p.rps);
+  else
+    hipLaunchKernelGGL((attend_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, s, ws.part_acc, ws.part_ml,
+                       reinterpret_cast<uint16_t *>(a.out), a.lse, a.q_tokens, a.n_q_heads, a.n_kv_heads, p.n_mt,
+                       p.n_split, p.rps);
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const msa_attend_args &a, float *part_acc, float *part_ml, hipStream_t s) {
-  return a.head_dim == 128 ? launch_attend_t<128>(a, part_acc, part_ml, s)
-                           : launch_attend_t<64>(a, part_acc, part_ml, s);
+hipError_t launch_attend(const msa_attend_args &a, const AttendWs &ws, hipStream_t s) {
+  const bool pre = ws.rot_k != nullptr && MSA_ATT_PREROT;
+  if (a.head_dim == 128)
+    return pre ? launch_attend_t<128, true>(a, ws, s) : launch_attend_t<128, false>(a, ws, s);
+  return pre ? launch_attend_t<64, true>(a, ws, s) : launch_attend_t<64, false>(a, ws, s);
 }
 
 }  // namespace msa

@@ -280,7 +280,7 @@ size_t msa_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head
     for (int32_t hkv = 1; hkv <= n_q_heads; ++hkv)
       if (n_q_heads % hkv == 0 && n_q_heads / hkv <= 16)
         need = std::max(need, attend_ws_layout(batch, 1, n_q_heads, hkv, head_dim, mem_cap, local_cap, nullptr,
-                                               nullptr, nullptr));
+                                               nullptr));
   return need;
 }
 
@@ -330,13 +330,13 @@ int msa_sparse_decode(const msa_decode_args *a, void *stream) {
     t.prof_event_begin = a->prof_event_begin;
     t.prof_event_end = a->prof_event_end;
     const size_t need = attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap,
-                                         nullptr, nullptr, nullptr);
+                                         nullptr, nullptr);
     if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
       return fail(MSA_ERR_WORKSPACE, "msa_sparse_decode: workspace needs %zu bytes (16-byte aligned), got %zu",
                   need, a->workspace ? a->workspace_bytes : (size_t)0);
-    attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap, a->workspace,
-                     &part_acc, &part_ml);
-    hipError_t e = launch_attend(t, part_acc, part_ml, reinterpret_cast<hipStream_t>(stream));
+    AttendWs aws;
+    attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap, a->workspace, &aws);
+    hipError_t e = launch_attend(t, aws, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_decode launch");
   }
   int32_t n_split = 0;
@@ -358,8 +358,7 @@ size_t msa_attend_workspace_bytes(int32_t batch, int32_t q_tokens, int32_t n_q_h
       n_q_heads / n_kv_heads > 16 || !dim_ok(head_dim) || mem_cap < 0 || local_cap < 0 ||
       (int64_t)mem_cap + local_cap > (1LL << 30))
     return 0;
-  return attend_ws_layout(batch, q_tokens, n_q_heads, n_kv_heads, head_dim, mem_cap, local_cap, nullptr, nullptr,
-                          nullptr);
+  return attend_ws_layout(batch, q_tokens, n_q_heads, n_kv_heads, head_dim, mem_cap, local_cap, nullptr, nullptr);
 }
 
 int msa_sparse_attend(const msa_attend_args *a, void *stream) {
@@ -385,14 +384,14 @@ int msa_sparse_attend(const msa_attend_args *a, void *stream) {
       (a->local_k && !aligned16(a->local_k)) || (a->local_v && !aligned16(a->local_v)))
     return fail(MSA_ERR_INVALID_ARG, "msa_sparse_attend: q, out and K/V tensors must be 16-byte aligned");
   const size_t need = attend_ws_layout(a->batch, a->q_tokens, a->n_q_heads, a->n_kv_heads, a->head_dim,
-                                       a->mem_cap, a->local_cap, nullptr, nullptr, nullptr);
+                                       a->mem_cap, a->local_cap, nullptr, nullptr);
   if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
     return fail(MSA_ERR_WORKSPACE, "msa_sparse_attend: workspace needs %zu bytes (16-byte aligned), got %zu",
                 need, a->workspace ? a->workspace_bytes : (size_t)0);
-  float *part_acc = nullptr, *part_ml = nullptr;
+  AttendWs aws;
   attend_ws_layout(a->batch, a->q_tokens, a->n_q_heads, a->n_kv_heads, a->head_dim, a->mem_cap, a->local_cap,
-                   a->workspace, &part_acc, &part_ml);
-  hipError_t e = launch_attend(*a, part_acc, part_ml, reinterpret_cast<hipStream_t>(stream));
+                   a->workspace, &aws);
+  hipError_t e = launch_attend(*a, aws, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_attend launch");
 }
 

@@ -153,8 +153,15 @@ struct AttendPlan {
 };
 void attend_plan(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t mem_cap, int32_t local_cap,
                  AttendPlan *p);
+// Attention workspace: split partials, and the local keys rotated once when
+// several query tiles per KV head read them (else rot_k is null).
+struct AttendWs {
+  float *part_acc;
+  float *part_ml;
+  uint16_t *rot_k;         // [B, local_cap, Hkv, D] bf16 or null
+};
 size_t attend_ws_layout(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t d, int32_t mem_cap,
-                        int32_t local_cap, void *base, float **part_acc, float **part_ml);
-hipError_t launch_attend(const msa_attend_args &a, float *part_acc, float *part_ml, hipStream_t s);
+                        int32_t local_cap, void *base, AttendWs *ws);
+hipError_t launch_attend(const msa_attend_args &a, const AttendWs &ws, hipStream_t s);
 
 }  // namespace msa
