@@ -42,6 +42,18 @@ constexpr int kWaves = kDocsPerBlock / 64;   // waves per workgroup
 constexpr int kSortCap = kMaxTopK;           // keys the final selection can order in LDS
 constexpr int kFastTopK = 64;                // k up to this uses the block-maximum bound
 constexpr int kBallotLists = 16;             // block maxima per lane in the ballot threshold (<= 1024 blocks)
+constexpr int kNarrow = 128;                 // block maxima at or above the lane bound searched in two lists
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o, 64));
+  return x;
+}
 
 __device__ void bitonic_desc(uint64_t *key, int n) {  // n a power of two; all threads call
   for (int size = 2; size <= n; size <<= 1) {
@@ -72,6 +84,22 @@ __device__ __forceinline__ int rank_of(const uint64_t *key, int n, uint64_t x, i
 
 __device__ __forceinline__ uint64_t doc_key(float score, int d) {
   return ((uint64_t)score_key(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)d);
+}
+
+// f(key) for every document d = tid, tid + blockDim, ... with eight loads
+// in flight per thread: unconditional loads of clamped indices (a load under
+// a branch is waited for before the branch joins)
+template <typename F>
+__device__ __forceinline__ void for_doc_keys(const float *ds, int n_docs, F f) {
+  const int nt = blockDim.x;
+  for (int d0 = threadIdx.x; d0 < n_docs; d0 += 8 * nt) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ds[min(d0 + u * nt, n_docs - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (d0 + u * nt < n_docs) f(doc_key(v[u], d0 + u * nt));
+  }
 }
 
 __device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t n_pool) {
@@ -221,6 +249,8 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
   __shared__ uint64_t sel[kSortCap];
   __shared__ uint32_t hist[kWaves][256];
   __shared__ int top_blk[kFastTopK];
+  __shared__ uint32_t nar_key[kNarrow];
+  __shared__ int nar_blk[kNarrow];
   __shared__ uint64_t ranked[kFastTopK];
   __shared__ uint64_t s_thr;
   __shared__ int s_nb;
@@ -230,41 +260,114 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
   const int tid = threadIdx.x, wave = tid >> 6;
   const uint64_t *bm = blockmax + (int64_t)b * n_blocks;
   const float *ds = doc_scores + (int64_t)b * n_docs;
+  const int len_in = plan && append ? mem_len[b] : 0;   // read early; written at the end
 
   bool sorted = false;
   if (k <= kFastTopK && n_blocks <= kSortCap) {
     if (n_blocks <= 64 * kBallotLists) {
-      // Wave 0 finds the score half T of the bound bit by bit: each lane
-      // holds up to kBallotLists block maxima, and the count of maxima
-      // scoring >= a candidate is a sum of ballot popcounts (no barrier, no
-      // sort).  The blocks whose maximum scores >= T - k of them, more only
-      // where scores tie - hold every winner, all with keys >= T << 32.
+      // Wave 0 finds the score half T of the bound: the k-th largest block
+      // maximum (score bits only).  The blocks whose maximum scores >= T -
+      // k of them, more only where scores tie - hold every winner, all with
+      // keys >= T << 32.  Each lane holds up to kBallotLists maxima.
+      //  1. L, the k-th largest of the lane maxima, bounds T from below (k
+      //     lanes hold a maximum >= L), so only the maxima >= L matter;
+      //  2. those are compacted into LDS (if at most kNarrow of them) and T
+      //     is found bit by bit over them: the count of maxima >= a
+      //     candidate is a sum of ballot popcounts, and the bits above the
+      //     highest one where L and the largest maximum differ are already
+      //     fixed, since T lies between the two.
       if (wave == 0) {
         const int lane = tid & 63;
-        uint32_t sk[kBallotLists];
-#pragma unroll
-        for (int m = 0; m < kBallotLists; ++m) {
-          const int i = lane + 64 * m;
-          sk[m] = i < n_blocks ? (uint32_t)(bm[i] >> 32) : 0u;
-        }
-        uint32_t T = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = T | (1u << bit);
-          int cnt = 0;
-#pragma unroll
-          for (int m = 0; m < kBallotLists; ++m) cnt += __popcll(__ballot(sk[m] >= cand));
-          if (cnt >= k) T = cand;
-        }
         const uint64_t below = (1ull << lane) - 1ull;
-        int base = 0;
+        const int n_lists = (n_blocks + 63) / 64;
+        uint32_t sk[kBallotLists];
+        uint32_t lm = 0;
 #pragma unroll
         for (int m = 0; m < kBallotLists; ++m) {
           const int i = lane + 64 * m;
-          const bool take = i < n_blocks && sk[m] >= T;
-          const uint64_t mask = __ballot(take);
-          const int pos = base + __popcll(mask & below);
-          if (take && pos < kFastTopK) top_blk[pos] = i;
-          base += __popcll(mask);
+          const uint32_t x = (uint32_t)(bm[min(i, n_blocks - 1)] >> 32);   // unconditional, as below
+          sk[m] = i < n_blocks ? x : 0u;
+          lm = max(lm, sk[m]);
+        }
+        // (wave-uniform values are made scalar, so the bit loops below run on
+        // scalar registers and branches)
+        const uint32_t mx = __builtin_amdgcn_readfirstlane(wave_max_u32(lm));
+        // 1. L over one list, from the highest bit where the lane maxima differ
+        uint32_t L = 0;
+        {
+          const uint32_t mn = __builtin_amdgcn_readfirstlane(wave_min_u32(lm));
+          const int hb = mx == mn ? -1 : 31 - __builtin_clz(mx ^ mn);
+          L = hb < 0 ? mx : (hb == 31 ? 0u : (mx >> (hb + 1)) << (hb + 1));
+          for (int bit = hb; bit >= 0; --bit) {
+            const uint32_t cand = L | (1u << bit);
+            if (__popcll(__ballot(lm >= cand)) >= k) L = cand;
+          }
+        }
+        // 2. compaction of the maxima >= L (keys and block numbers)
+        int n_s = 0;
+#pragma unroll
+        for (int m = 0; m < kBallotLists; ++m) {
+          if (m < n_lists) {                               // uniform
+            const int i = lane + 64 * m;
+            const bool take = i < n_blocks && sk[m] >= L;
+            const uint64_t mask = __ballot(take);
+            const int pos = n_s + __popcll(mask & below);
+            if (take && pos < kNarrow) { nar_key[pos] = sk[m]; nar_blk[pos] = i; }
+            n_s += __popcll(mask);
+          }
+        }
+        // LDS operations of one wave complete in order; keep the compiler's too
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        uint32_t T = 0;
+        int base = 0;
+        if (n_s <= kNarrow) {
+          uint32_t nk[kNarrow / 64];
+          int nbk[kNarrow / 64];
+#pragma unroll
+          for (int m = 0; m < kNarrow / 64; ++m) {
+            const int i = lane + 64 * m;
+            nk[m] = i < n_s ? nar_key[i] : 0u;
+            nbk[m] = i < n_s ? nar_blk[i] : 0;
+          }
+          const int hb = L == mx ? -1 : 31 - __builtin_clz(L ^ mx);
+          T = hb < 0 ? L : (hb == 31 ? 0u : (L >> (hb + 1)) << (hb + 1));
+          for (int bit = hb; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int m = 0; m < kNarrow / 64; ++m) cnt += __popcll(__ballot(nk[m] >= cand));
+            if (cnt >= k) T = cand;
+          }
+#pragma unroll
+          for (int m = 0; m < kNarrow / 64; ++m) {
+            const bool take = lane + 64 * m < n_s && nk[m] >= T;
+            const uint64_t mask = __ballot(take);
+            const int pos = base + __popcll(mask & below);
+            if (take && pos < kFastTopK) top_blk[pos] = nbk[m];
+            base += __popcll(mask);
+          }
+        } else {
+          // many maxima tie near the bound: the same search over every list
+          for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int m = 0; m < kBallotLists; ++m)
+              if (m < n_lists) cnt += __popcll(__ballot(sk[m] >= cand));
+            if (cnt >= k) T = cand;
+          }
+#pragma unroll
+          for (int m = 0; m < kBallotLists; ++m) {
+            if (m < n_lists) {
+              const int i = lane + 64 * m;
+              const bool take = i < n_blocks && sk[m] >= T;
+              const uint64_t mask = __ballot(take);
+              const int pos = base + __popcll(mask & below);
+              if (take && pos < kFastTopK) top_blk[pos] = i;
+              base += __popcll(mask);
+            }
+          }
         }
         if (lane == 0) {
           s_nb = base;
@@ -291,19 +394,21 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
     const uint64_t thr = s_thr;
     if (nb <= kFastTopK) {
       // the documents of the selected blocks whose keys reach the bound:
-      // thread t takes position t of every block, eight blocks' loads in
+      // thread t takes position t of every block, sixteen blocks' loads in
       // flight before any is used (blockDim == kDocsPerBlock)
-      for (int j0 = 0; j0 < nb; j0 += 8) {
-        float v[8];
-        int dd[8];
+      for (int j0 = 0; j0 < nb; j0 += 16) {
+        float v[16];
+        int dd[16];
+        // unconditional loads of clamped indices: a load under a branch is
+        // waited for before the branch joins, which would serialize them
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const int blk = j0 + u < nb ? min(max(top_blk[j0 + u], 0), n_blocks - 1) : 0;
           dd[u] = j0 + u < nb ? blk * kDocsPerBlock + tid : n_docs;
-          v[u] = dd[u] < n_docs ? ds[dd[u]] : 0.f;
+          v[u] = ds[min(dd[u], n_docs - 1)];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           if (dd[u] < n_docs) {
             const uint64_t x = doc_key(v[u], dd[u]);
             if (x >= thr) {
@@ -327,10 +432,9 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
       for (int i = tid; i < kWaves * 256; i += blockDim.x) (&hist[0][0])[i] = 0;
       __syncthreads();
       const uint64_t prefix = s_prefix, mask = s_mask;
-      for (int d = tid; d < n_docs; d += blockDim.x) {
-        const uint64_t x = doc_key(ds[d], d);
+      for_doc_keys(ds, n_docs, [&](uint64_t x) {
         if ((x & mask) == prefix) atomicAdd(&hist[wave][(x >> shift) & 255u], 1u);
-      }
+      });
       __syncthreads();
       if (tid < 256) {
         uint32_t sum = 0;
@@ -353,13 +457,12 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
       __syncthreads();
     }
     const uint64_t thr = s_prefix;   // the k-th largest key exactly (keys are unique)
-    for (int d = tid; d < n_docs; d += blockDim.x) {
-      const uint64_t x = doc_key(ds[d], d);
+    for_doc_keys(ds, n_docs, [&](uint64_t x) {
       if (x >= thr) {
         const int pos = atomicAdd(&s_count, 1);
         if (pos < kSortCap) sel[pos] = x;
       }
-    }
+    });
     __syncthreads();
   }
   // Order the survivors.  At most one per thread: rank counting (a key's
@@ -390,6 +493,41 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
   }
   if (!plan) return;
   // ---- context assembly plan: documents in rank order while they fit ----
+  if (k <= 64) {
+    // one wave: rank r = lane; a document is placed iff the inclusive
+    // prefix of the row counts still fits (the counts are non-negative, so
+    // the first one that does not fit closes the plan for every later rank)
+    if (wave == 0) {
+      const int r = tid;
+      int64_t r0 = 0, pr = 0;
+      if (r < k) {
+        const int dd = min(max((int)(0xffffffffu - (uint32_t)(top[r] & 0xffffffffu)), 0), n_docs - 1);
+        r0 = clamp_row(pool_off[dd], n_pool);
+        const int64_t r1 = max(r0, clamp_row(pool_off[dd + 1], n_pool));
+        pr = min(r1 - r0, (int64_t)mem_cap + 1);
+      }
+      int64_t inc = pr;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up((long)inc, o, 64);
+        if (r >= o) inc += y;
+      }
+      const int64_t len0 = append ? max(0, min(len_in, mem_cap)) : 0;
+      const bool open = r < k && len0 + inc <= mem_cap;
+      GatherPlan p = {0, 0, 0};
+      if (open) {
+        p.src_row = r0;
+        p.rows = (int32_t)pr;
+        p.dst_row = (int32_t)(len0 + inc - pr);
+      }
+      if (r < k) plan[(int64_t)b * k + r] = p;
+      const uint64_t end = __ballot(open);                 // open ranks are a prefix
+      const int n_open = __popcll(end);
+      const int64_t len = n_open ? len0 + __shfl(inc, n_open - 1, 64) : len0;
+      if (r == 0) mem_len[b] = (int32_t)len;
+    }
+    return;
+  }
   __shared__ int32_t prow[kMaxTopK], pdst[kMaxTopK];
   __syncthreads();                       // top[] is reused below
   for (int r = tid; r < k; r += blockDim.x) {   // every rank's offsets loaded in parallel
@@ -401,7 +539,7 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
   }
   __syncthreads();
   if (tid == 0) {                        // prefix over LDS only
-    int64_t len = append ? max(0, min(mem_len[b], mem_cap)) : 0;
+    int64_t len = append ? max(0, min(len_in, mem_cap)) : 0;
     bool open = true;
     for (int r = 0; r < k; ++r) {
       open = open && len + prow[r] <= mem_cap;

@@ -382,6 +382,36 @@ def test_route_document_path_ties_and_whole_tiles():
     assert all(idx[b, :5].tolist() == twins for b in range(12))
 
 
+def test_route_top_k_bound_when_block_maxima_tie():
+    """250,000 one-row documents (977 blocks of 256): 300 blocks share one
+    tied maximum and the 16 blocks above it all sit in the same lane of the
+    bound's search (blocks 0, 64, ..., 960), so more than 128 block maxima
+    reach the lane bound and the selection takes its every-list search; the
+    winners are exactly the 16 planted documents, in score order."""
+    g = torch.Generator().manual_seed(41)
+    n_docs = 250_000
+    off = np.arange(n_docs + 1, dtype=np.int64)
+    kr = torch.randn(n_docs, 1, 128, generator=g)
+    q = torch.randn(128, generator=g)
+    u = torch.randn(128, generator=g)
+    qh = q / q.norm()
+    u = u - (u @ qh) * qh
+    uh = u / u.norm()
+    row = lambda c: c * qh + (1 - c * c) ** 0.5 * uh  # noqa: E731  (cosine c with q)
+    tied = [b for b in range(977) if b % 64 != 0][:300]
+    for b in tied:
+        kr[256 * b + 5, 0] = row(0.6)
+    high = [256 * 64 * j + 7 for j in range(16)]
+    for j, d in enumerate(high):
+        kr[d, 0] = row(0.7 + 0.01 * j)
+    kr = kr.to(torch.bfloat16).to(DEV)
+    qr = q.reshape(1, 1, 1, 128).to(torch.bfloat16).to(DEV)
+    _say("route: 250,000 documents, 300 tied block maxima under 16 in one lane")
+    idx, ref = _route_check(kr, off, qr, 16, "tied block maxima")
+    assert idx[0].tolist() == high[::-1]
+    _route_both_layouts(qr, kr, off, 16, "tied block maxima, tiled")
+
+
 def test_route_all_documents_and_degenerate_rows():
     g = torch.Generator().manual_seed(6)
     kr, off = _ragged_bank(g, 37, 3, 8, 128, torch.bfloat16)
