@@ -31,7 +31,7 @@ namespace {
 #define MSA_POOL_VSPLIT 1
 #endif
 #ifndef MSA_POOL_UNROLL
-#define MSA_POOL_UNROLL 4
+#define MSA_POOL_UNROLL 8
 #endif
 constexpr int kUnroll = MSA_POOL_UNROLL;   // tokens in flight per lane (x2 loads for K)
 
