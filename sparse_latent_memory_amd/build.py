@@ -1,9 +1,11 @@
-"""Build libmsa.so (HIP, gfx950) in-tree with hipcc.
+"""Build libmsa.so (HIP, gfx950) in-tree with hipcc, and beside it
+libmsa_readref.so, the reference streaming-read kernel that bench.py times
+against the bank scan (measurement only, not part of libmsa).
 
     python -m sparse_latent_memory_amd.build [-v]
 
 Every call recompiles; objects go to _build/ next to the package and the
-library to sparse_latent_memory_amd/libmsa.so.
+libraries to sparse_latent_memory_amd/.
 """
 
 import os
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(HERE)
 SOURCES = ["msa_api.hip", "pool.hip", "route.hip", "route_scan.hip", "route_scan_wide.hip", "route_select.hip",
            "decode.hip", "attend.hip"]
 LIB = os.path.join(HERE, "libmsa.so")
+READREF_SOURCE = "read_ref.hip"
+READREF_LIB = os.path.join(HERE, "libmsa_readref.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -53,7 +57,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose=False, jobs=4):
-    """Compile every HIP source for gfx950 and link libmsa.so."""
+    """Compile every HIP source for gfx950 and link libmsa.so and
+    libmsa_readref.so."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -62,11 +67,14 @@ def build(verbose=False, jobs=4):
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([hipcc, *CFLAGS, "-c", os.path.join(HERE, "csrc", src), "-o", obj])
+    ref_obj = os.path.join(BUILD_DIR, READREF_SOURCE.replace(".hip", ".o"))
+    cmds.append([hipcc, *CFLAGS, "-c", os.path.join(HERE, "csrc", READREF_SOURCE), "-o", ref_obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (READREF_LIB, [ref_obj])):
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -35,6 +35,27 @@ def test_library_built_and_exports_every_declared_symbol():
         assert set(declared) <= exported
 
 
+def test_read_reference_library_exports_its_declared_symbol_and_checks_arguments():
+    """libmsa_readref.so (the streaming-read reference bench.py times beside
+    the scan) exports what include/msa_readref.h declares and refuses bad
+    arguments before any launch."""
+    from sparse_latent_memory_amd import readref
+    text = open(os.path.join(ROOT, "include", "msa_readref.h")).read()
+    declared = set(re.findall(r"^\s*int\s+(msa_\w+)\s*\(", text, re.M))
+    assert declared == set(readref.EXPORTS)
+    lib = readref.load()
+    for name in declared:
+        assert hasattr(lib, name), name
+    f = lib.msa_ref_read_tiles
+    sink, buf = ctypes.c_void_p(256), ctypes.c_void_p(4096)   # never dereferenced: every call is refused
+    assert f(None, 32768, 1, 1, sink, None, None, None) == -1
+    assert f(buf, 32768, 1, 1, None, None, None, None) == -1
+    assert f(buf, 32768 + 16, 1, 1, sink, None, None, None) == -1      # not whole tiles
+    assert f(buf, 0, 1, 1, sink, None, None, None) == -1
+    assert f(buf, 32768, 0, 1, sink, None, None, None) == -1           # empty grid
+    assert f(ctypes.c_void_p(4100), 32768, 1, 1, sink, None, None, None) == -1   # misaligned
+
+
 def test_version():
     assert _lib.load().msa_version() == 100
 
