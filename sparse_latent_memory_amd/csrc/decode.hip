@@ -38,8 +38,9 @@ __device__ __forceinline__ float wave_max(float x) {
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
   return x;
 }
+// fp32 at D = 128 stages 66 KiB of K/V per workgroup in LDS: two fit on a CU
 template <typename T, int D>
-__global__ __launch_bounds__(256, 3) void decode_split_kernel(
+__global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 2 : 3) void decode_split_kernel(
     const T *__restrict__ q, const T *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
     const T *__restrict__ local_k, const T *__restrict__ local_v, const int32_t *__restrict__ local_len,
     const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc, float *__restrict__ part_ml,
