@@ -93,6 +93,21 @@ __global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict_
 // the MALL; workgroups are dispatched round-robin over the 8 XCDs, which the
 // XCD-major logical id below follows.
 constexpr int kWideWaves = 8;
+
+// One doubling step of the segmented max over the 16 rows of a tile (lane
+// column = row): row r takes row r + SH's running max while no document
+// starts in rows r+1 .. r+SH.  The value of row r + SH arrives through a DPP
+// row shift (row_shl, within each 16-lane row), so the step costs vector
+// instructions only, no LDS permute.
+template <int SH>
+__device__ __forceinline__ void seg_step(f32x4 &v, int col, uint32_t bits) {
+  const bool same = col + SH < 16 && ((bits >> (col + 1)) & ((1u << SH) - 1u)) == 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float u = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[i]), 0x100 + SH, 0xf, 0xf, false));
+    v[i] = same ? fmaxf(v[i], u) : v[i];
+  }
+}
 // Bank layouts of the wide scan: row-major, tiled (plain loads: several
 // query chunks share each bank tile through L2) and tiled with non-temporal
 // loads (one query chunk: every tile is read once; measured 13-14% faster at
@@ -207,15 +222,10 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
     for (int mt = 0; mt < NM; ++mt) {
       if (mt >= nm) break;                // (uniform)
       f32x4 v = acc[mt];
-#pragma unroll
-      for (int sh = 1; sh < 16; sh <<= 1) {
-        const bool same = col + sh < 16 && ((bits >> (col + 1)) & ((1u << sh) - 1u)) == 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float u = __shfl_down(v[i], sh, 16);
-          v[i] = same ? fmaxf(v[i], u) : v[i];
-        }
-      }
+      seg_step<1>(v, col, bits);
+      seg_step<2>(v, col, bits);
+      seg_step<4>(v, col, bits);
+      seg_step<8>(v, col, bits);
       if (run_start && row < n_pool) {
         const int b0 = (t0 + mt) * 16 + 4 * grp;
         float *dst = starts_doc ? doc_part + (int64_t)d * qstride + b0 : tile_cont + tile * qstride + b0;
