@@ -243,7 +243,7 @@ def main():
     log(f"bank: {n_docs} docs, {bank_tokens} tokens, {n_pool} pooled rows")
     kr = synth.pooled_router_bank(cfg, lens, device=dev)
     lay = args.kr_layout
-    bank, rkw = _router_bank(kr, n_pool, lay)      # what the scan reads
+    bank, rkw = _router_bank(kr, pool_off, lay)    # what the scan reads
     host_kv = synth.pooled_content_bank(cfg, lens, device=dev, pin=True)
     pool_off_d = torch.as_tensor(pool_off, device=dev)
     pool_off_h = torch.as_tensor(pool_off)
@@ -391,6 +391,7 @@ def main():
             "pooled_rows": n_pool,
             "global_batch": cfg.batch,
             "kr_layout": lay,
+            "doc_map": "built once with the bank (msa_doc_map) and passed to every route call",
         },
         "roofline": {
             "kernel": f"route bank scan ({SCAN_KERNELS[lay]})",
@@ -436,9 +437,14 @@ class StreamEvents:
         return a.elapsed_time(b)
 
 
-def _router_bank(kr, n_pool, lay):
-    """The router bank in the layout the scan reads, and route()'s keywords for it."""
-    return (synth.tile_router_bank(kr) if lay == "tiled" else kr), {"kr_layout": lay, "n_pool": n_pool}
+def _router_bank(kr, off, lay):
+    """The router bank in the layout the scan reads, and route()'s keywords
+    for it: the layout, the row count and the bank's document map, built
+    once here (msa_doc_map) as part of the bank, like its layout."""
+    n_pool = int(off[-1])
+    dmap = msa.doc_map(torch.as_tensor(off, device=kr.device), n_pool)
+    return (synth.tile_router_bank(kr) if lay == "tiled" else kr), {"kr_layout": lay, "n_pool": n_pool,
+                                                                    "doc_map": dmap}
 
 
 def _supporting_line(metric, value, unit, workload, roofline, extra, higher=True, kr_layout=None):
@@ -463,7 +469,7 @@ def workload_interleave(args, dev):
     off = synth.row_offsets(lens, cfg.pool)
     n_docs, n_pool = len(lens), int(off[-1])
     log(f"interleave bank: {n_docs} docs, {int(lens.sum())} tokens, {n_pool} pooled rows")
-    kr, rkw = _router_bank(synth.pooled_router_bank(cfg, lens, device=dev), n_pool, args.kr_layout)
+    kr, rkw = _router_bank(synth.pooled_router_bank(cfg, lens, device=dev), off, args.kr_layout)
     host_kv = synth.pooled_content_bank(cfg, lens, device=dev, pin=True)
     off_d = torch.as_tensor(off, device=dev)
     k, B = cfg.top_k, cfg.batch
@@ -656,7 +662,7 @@ def workload_needles(args, dev):
     kr = synth.pooled_router_bank(cfg, lens, device=dev)
     qr = synth.router_queries(cfg, device=dev)
     needles = synth.plant_needles(cfg, qr, kr, off)
-    kr, rkw = _router_bank(kr, n_pool, args.kr_layout)
+    kr, rkw = _router_bank(kr, off, args.kr_layout)
     off_d = torch.as_tensor(off, device=dev)
     k = cfg.top_k
     rws = torch.empty(msa.route_workspace_bytes(torch.bfloat16, cfg.batch, 1, cfg.n_router_heads, cfg.router_dim,

@@ -220,6 +220,10 @@ typedef struct {
    * and its end, and add no packet to the queue; NULL to skip */
   void *prof_event_begin;
   void *prof_event_end;
+  /* optional: the document map of doc_pool_off from msa_doc_map (below),
+   * used by the document path instead of building it in the workspace on
+   * every call; 16-byte aligned.  NULL to build it per call. */
+  const void *doc_map;
 } msa_route_args;
 
 int msa_route(const msa_route_args *args, void *stream);
@@ -228,6 +232,24 @@ int msa_route(const msa_route_args *args, void *stream);
 size_t msa_route_workspace_bytes(int32_t dtype, int32_t batch, int32_t q_tokens,
                                  int32_t n_router_heads, int32_t router_dim,
                                  int32_t n_docs, int64_t n_pool, int32_t top_k);
+
+/* Document map of a router bank: an optional input of msa_route.
+ * The document path of msa_route (one token per query on the matrix-core
+ * scans) reduces each 16-row tile of the bank per document inside the scan;
+ * for that it needs, per tile t (n_tiles = ceil(n_pool / 16)), the document
+ * holding row 16 t and a bit per row 16 t + r (r < 16) that starts a
+ * document or is row n_pool.  This depends on doc_pool_off alone (the
+ * document-per-row reading of the routing passage quoted above), so a bank
+ * routed many times can build it once: msa_doc_map writes it to doc_map,
+ * device memory of msa_doc_map_bytes(n_pool) bytes, 16-byte aligned (layout:
+ * n_tiles int32 document numbers, then, at the next multiple of 256 bytes,
+ * n_tiles uint32 row masks), enqueued on `stream`.  The map describes exactly
+ * the offsets it was built from; routing with a map of other offsets gives
+ * wrong scores.  Returns MSA_ERR_INVALID_ARG for NULL pointers, n_docs < 1,
+ * n_pool < n_docs or too small a buffer (nothing enqueued). */
+size_t msa_doc_map_bytes(int64_t n_pool);
+int msa_doc_map(const int64_t *doc_pool_off, int32_t n_docs, int64_t n_pool, void *doc_map,
+                size_t doc_map_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Stage 3 - one sparse decode-attention step.

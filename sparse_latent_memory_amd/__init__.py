@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     attend_workspace_bytes,
     bank_rows,
     decode_workspace_bytes,
+    doc_map,
+    doc_map_bytes,
     load,
     pool_encode,
     route,
@@ -21,5 +23,6 @@ from ._lib import (  # noqa: F401
     sparse_decode,
 )
 
-__all__ = ["Assembly", "MSAError", "attend_workspace_bytes", "bank_rows", "decode_workspace_bytes", "load", "pool_encode",
-           "route", "route_workspace_bytes", "sparse_attend", "sparse_decode", "synth"]
+__all__ = ["Assembly", "MSAError", "attend_workspace_bytes", "bank_rows", "decode_workspace_bytes", "doc_map",
+           "doc_map_bytes", "load", "pool_encode", "route", "route_workspace_bytes", "sparse_attend", "sparse_decode",
+           "synth"]

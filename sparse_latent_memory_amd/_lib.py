@@ -52,7 +52,7 @@ class RouteArgs(ctypes.Structure):
         ("host_kv", P), ("host_doc_pool_off", P), ("kv_dtype", I32), ("n_kv_heads", I32), ("head_dim", I32),
         ("mem_cap", I32), ("append", I32), ("gather_mode", I32), ("mem_kv", P), ("mem_len", P), ("host_topk_idx", P),
         ("host_mem_len", P), ("host_mem_docs", P), ("copy_stream", P),
-        ("prof_event_begin", P), ("prof_event_end", P),
+        ("prof_event_begin", P), ("prof_event_end", P), ("doc_map", P),
     ]
 
 
@@ -78,7 +78,8 @@ class AttendArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ("msa_pool_encode", "msa_route", "msa_route_workspace_bytes", "msa_sparse_decode",
+EXPORTS = ("msa_pool_encode", "msa_route", "msa_route_workspace_bytes", "msa_doc_map_bytes", "msa_doc_map",
+           "msa_sparse_decode",
            "msa_decode_workspace_bytes", "msa_sparse_attend", "msa_attend_workspace_bytes", "msa_last_error",
            "msa_version")
 
@@ -103,6 +104,10 @@ def load(path=None):
     lib.msa_sparse_decode.restype = ctypes.c_int
     lib.msa_route_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I64, I32]
     lib.msa_route_workspace_bytes.restype = ctypes.c_size_t
+    lib.msa_doc_map_bytes.argtypes = [I64]
+    lib.msa_doc_map_bytes.restype = ctypes.c_size_t
+    lib.msa_doc_map.argtypes = [P, I32, I64, P, ctypes.c_size_t, P]
+    lib.msa_doc_map.restype = ctypes.c_int
     lib.msa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.msa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_sparse_attend.argtypes = [ctypes.POINTER(AttendArgs), P]
@@ -256,10 +261,12 @@ class Assembly:
 
 
 def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, topk_score=None,
-          workspace=None, assembly=None, stream=None, prof_events=None, kr_layout="rows", n_pool=None):
+          workspace=None, assembly=None, stream=None, prof_events=None, kr_layout="rows", n_pool=None,
+          doc_map=None):
     """msa_route.  qr: [B, Tq, Hr, dr]; kr_pooled: the router bank in
     `kr_layout` ("rows": [n_pool, Hr, dr]; "tiled": whole 16-row tiles,
-    n_pool given); doc_pool_off: int64 device [n_docs+1].  Returns
+    n_pool given); doc_pool_off: int64 device [n_docs+1]; doc_map: optional,
+    doc_map(doc_pool_off, n_pool)'s output for these offsets.  Returns
     (topk_idx, topk_score, doc_scores)."""
     b, tq, hr, dr = qr.shape
     lay = _layout_code(kr_layout)
@@ -305,8 +312,30 @@ def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, to
         a.copy_stream = _stream(cs)
     if prof_events is not None:
         a.prof_event_begin, a.prof_event_end = prof_events
+    if doc_map is not None:
+        if doc_map.numel() * doc_map.element_size() < doc_map_bytes(n_pool):
+            raise ValueError(f"doc_map holds {doc_map.numel() * doc_map.element_size()} bytes, "
+                             f"{doc_map_bytes(n_pool)} needed")
+        a.doc_map = _dptr(doc_map, "doc_map")
     _check(load().msa_route(ctypes.byref(a), _stream(stream)))
     return topk_idx, topk_score, doc_scores
+
+
+def doc_map_bytes(n_pool):
+    return int(load().msa_doc_map_bytes(n_pool))
+
+
+def doc_map(doc_pool_off, n_pool, out=None, stream=None):
+    """msa_doc_map: the document map of a bank (doc_pool_off int64 device
+    [n_docs+1]) into `out` (uint8 device, doc_map_bytes(n_pool) bytes), for
+    route(..., doc_map=...).  Returns out."""
+    n_docs = doc_pool_off.numel() - 1
+    nbytes = doc_map_bytes(n_pool)
+    if out is None:
+        out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=doc_pool_off.device)
+    _check(load().msa_doc_map(_dptr(doc_pool_off, "doc_pool_off"), n_docs, n_pool, _dptr(out, "doc_map"),
+                              out.numel() * out.element_size(), _stream(stream)))
+    return out
 
 
 # --------------------------------------------------------------------------

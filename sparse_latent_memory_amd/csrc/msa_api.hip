@@ -159,6 +159,26 @@ size_t msa_route_workspace_bytes(int32_t dtype, int32_t batch, int32_t q_tokens,
                          nullptr);
 }
 
+size_t msa_doc_map_bytes(int64_t n_pool) {
+  if (n_pool < 1) return 0;
+  return doc_map_bits_offset(n_pool) + (((size_t)4 * (size_t)((n_pool + 15) / 16) + 255) & ~(size_t)255);
+}
+
+int msa_doc_map(const int64_t *doc_pool_off, int32_t n_docs, int64_t n_pool, void *doc_map, size_t doc_map_bytes,
+                void *stream) {
+  if (!doc_pool_off || !doc_map) return fail(MSA_ERR_INVALID_ARG, "msa_doc_map: NULL pointer");
+  if (n_docs < 1 || n_pool < n_docs || n_docs > 0x7ffffffe)
+    return fail(MSA_ERR_INVALID_ARG, "msa_doc_map: need 1 <= n_docs <= n_pool");
+  if (!aligned16(doc_map) || doc_map_bytes < msa_doc_map_bytes(n_pool))
+    return fail(MSA_ERR_INVALID_ARG, "msa_doc_map: doc_map needs %zu bytes (16-byte aligned), got %zu",
+                msa_doc_map_bytes(n_pool), doc_map_bytes);
+  char *m = reinterpret_cast<char *>(doc_map);
+  const hipError_t e = launch_doc_map(doc_pool_off, n_docs, n_pool, reinterpret_cast<int32_t *>(m),
+                                      reinterpret_cast<uint32_t *>(m + doc_map_bits_offset(n_pool)),
+                                      reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_doc_map launch");
+}
+
 int msa_route(const msa_route_args *a, void *stream) {
   if (!a) return fail(MSA_ERR_INVALID_ARG, "msa_route: args is NULL");
   if (!dtype_ok(a->dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_route: bad dtype %d", a->dtype);
@@ -186,6 +206,8 @@ int msa_route(const msa_route_args *a, void *stream) {
   if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
     return fail(MSA_ERR_WORKSPACE, "msa_route: workspace needs %zu bytes (16-byte aligned), got %zu", need,
                 a->workspace ? a->workspace_bytes : (size_t)0);
+  if (a->doc_map && !aligned16(a->doc_map))
+    return fail(MSA_ERR_INVALID_ARG, "msa_route: doc_map must be 16-byte aligned");
   const bool assemble = a->host_kv != nullptr;
   const bool kernel_gather = assemble && a->gather_mode == MSA_GATHER_KERNEL;
   void *host_kv_dev = nullptr;
@@ -222,6 +244,12 @@ int msa_route(const msa_route_args *a, void *stream) {
   RouteWs ws;
   route_ws_layout(a->dtype, a->batch, a->q_tokens, a->n_router_heads, a->router_dim, a->n_docs, a->n_pool,
                   a->top_k, a->workspace, &ws);
+  if (a->doc_map) {
+    char *m = reinterpret_cast<char *>(const_cast<void *>(a->doc_map));
+    ws.tile_doc = reinterpret_cast<int32_t *>(m);
+    ws.tile_bits = reinterpret_cast<uint32_t *>(m + doc_map_bits_offset(a->n_pool));
+    ws.map_given = 1;
+  }
   hipError_t e = launch_route(*a, ws, host_kv_dev, s);
   if (e != hipSuccess) return hip_fail(e, "msa_route launch");
   if (!assemble || kernel_gather) return MSA_OK;

@@ -49,6 +49,7 @@ struct RouteWs {  // carved out of the caller's workspace
   int32_t n_parts;         // partial token maxima per query in row_score (wide scan), else 1
   int32_t qstride;         // query stride of doc_part / tile_cont: a multiple of 16 on the wide
                            // scan, B rounded up to 4 on the narrow one; 0 on the row path
+  int32_t map_given;       // tile_doc / tile_bits point into a caller's document map
 };
 // Routing kernels.  The bank scan writes row_score[b, j] (max over query b's
 // tokens of the head-mean cosine) or, on the document path, per-document
@@ -130,7 +131,12 @@ hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, const Ro
 hipError_t launch_scan_valu(const msa_route_args &a, const float *qhat, float *row_score, hipStream_t s);
 // document map of the document path, per-document scores, exact top-k,
 // assembly plan and device-side gather (route_select.hip)
-hipError_t launch_doc_map(const msa_route_args &a, const RouteWs &ws, hipStream_t s);
+hipError_t launch_doc_map(const int64_t *pool_off, int32_t n_docs, int64_t n_pool, int32_t *tile_doc,
+                          uint32_t *tile_bits, hipStream_t s);
+// the document map's layout (msa_doc_map): tile_doc at 0, tile_bits here
+inline size_t doc_map_bits_offset(int64_t n_pool) {
+  return ((size_t)4 * (size_t)((n_pool + 15) / 16) + 255) & ~(size_t)255;
+}
 hipError_t launch_select(const msa_route_args &a, const RouteWs &ws, const void *host_kv_dev, hipStream_t s);
 
 size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t hr, int32_t dr,

@@ -90,6 +90,7 @@ size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t h
     ws->n_blocks = n_blocks;
     ws->n_parts = n_parts;
     ws->qstride = qstride;
+    ws->map_given = 0;
   }
   return off;
 }
@@ -99,13 +100,17 @@ hipError_t launch_route(const msa_route_args &a, const RouteWs &ws, const void *
   hipError_t e = hipSuccess;
   // the scan launchers attach a.prof_event_begin / _end to the scan kernel
   if (narrow_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
-    if (ws.qstride > 0 && (e = launch_doc_map(a, ws, s)) != hipSuccess) return e;
+    if (ws.qstride > 0 && !ws.map_given &&
+        (e = launch_doc_map(a.doc_pool_off, a.n_docs, a.n_pool, ws.tile_doc, ws.tile_bits, s)) != hipSuccess)
+      return e;
     e = launch_scan_narrow(a, ws, s);
   } else {
     if ((e = launch_prep_unit(a, ws.qhat, s)) != hipSuccess) return e;
     if (wide_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
       if ((e = launch_prep_wide(a, ws.qhat, ws.wide_frag, s)) != hipSuccess) return e;
-      if (ws.qstride > 0 && (e = launch_doc_map(a, ws, s)) != hipSuccess) return e;
+      if (ws.qstride > 0 && !ws.map_given &&
+          (e = launch_doc_map(a.doc_pool_off, a.n_docs, a.n_pool, ws.tile_doc, ws.tile_bits, s)) != hipSuccess)
+        return e;
       e = launch_scan_wide(a, ws.wide_frag, ws, s);
     } else {
       e = launch_scan_valu(a, ws.qhat, ws.row_score, s);

@@ -589,9 +589,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
 
 }  // namespace
 
-hipError_t launch_doc_map(const msa_route_args &a, const RouteWs &ws, hipStream_t s) {
-  hipLaunchKernelGGL(doc_map_kernel, dim3((a.n_docs + 255) / 256), dim3(256), 0, s, a.doc_pool_off, ws.tile_doc,
-                     ws.tile_bits, a.n_docs, a.n_pool);
+hipError_t launch_doc_map(const int64_t *pool_off, int32_t n_docs, int64_t n_pool, int32_t *tile_doc,
+                          uint32_t *tile_bits, hipStream_t s) {
+  hipLaunchKernelGGL(doc_map_kernel, dim3((n_docs + 255) / 256), dim3(256), 0, s, pool_off, tile_doc, tile_bits,
+                     n_docs, n_pool);
   return hipGetLastError();
 }
 

@@ -56,6 +56,25 @@ def test_read_reference_library_exports_its_declared_symbol_and_checks_arguments
     assert f(ctypes.c_void_p(4100), 32768, 1, 1, sink, None, None, None) == -1   # misaligned
 
 
+def test_doc_map_size_and_argument_checks():
+    """msa_doc_map_bytes: n_tiles int32 then, 256-byte aligned, n_tiles
+    uint32; msa_doc_map refuses NULL pointers, bad counts and a short or
+    misaligned buffer before launching anything."""
+    lib = _lib.load()
+    assert lib.msa_doc_map_bytes(0) == 0
+    assert lib.msa_doc_map_bytes(17) == 512                 # 2 tiles: 8 B -> 256, twice
+    assert lib.msa_doc_map_bytes(16 * 64) == 512            # 64 tiles: 256 B each
+    assert lib.msa_doc_map_bytes(16 * 65) == 1024
+    off, buf = ctypes.c_void_p(4096), ctypes.c_void_p(8192)  # never dereferenced: every call is refused
+    assert lib.msa_doc_map(None, 4, 100, buf, 4096, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_doc_map(off, 4, 100, None, 4096, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_doc_map(off, 0, 100, buf, 4096, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_doc_map(off, 101, 100, buf, 4096, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_doc_map(off, 4, 100, buf, 256, None) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_doc_map(off, 4, 100, ctypes.c_void_p(8200), 4096, None) == _lib.MSA_ERR_INVALID_ARG
+    assert b"doc_map" in lib.msa_last_error()
+
+
 def test_version():
     assert _lib.load().msa_version() == 100
 

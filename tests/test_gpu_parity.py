@@ -382,6 +382,71 @@ def test_route_document_path_ties_and_whole_tiles():
     assert all(idx[b, :5].tolist() == twins for b in range(12))
 
 
+def _doc_map_reference(off):
+    """The document map written out from its definition: per 16-row tile,
+    the document holding the tile's first row, and bit r set where row
+    16 t + r starts a document or is row n_pool."""
+    off = np.asarray(off, dtype=np.int64)
+    n_pool = int(off[-1])
+    n_tiles = (n_pool + 15) // 16
+    starts = set(off[:-1].tolist()) | {n_pool}
+    doc = np.searchsorted(off, 16 * np.arange(n_tiles), side="right") - 1
+    bits = np.array([sum(1 << r for r in range(16) if 16 * t + r in starts) for t in range(n_tiles)],
+                    dtype=np.uint32)
+    return doc.astype(np.int32), bits
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_doc_map_matches_its_definition(seed):
+    """msa_doc_map, bit for bit against the map written out in Python: 400
+    documents of 1 to 70 rows (many starts in one tile, documents spanning
+    many tiles) and a bank that ends inside its last tile."""
+    g = torch.Generator().manual_seed(70 + seed)
+    rows = np.where(torch.rand(400, generator=g).numpy() < 0.3,
+                    torch.randint(17, 71, (400,), generator=g).numpy(),
+                    torch.randint(1, 4, (400,), generator=g).numpy())
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    n_pool = int(off[-1])
+    _say(f"doc map: 400 documents, {n_pool} rows")
+    m = msa.doc_map(_dev(off), n_pool)
+    torch.cuda.synchronize()
+    n_tiles = (n_pool + 15) // 16
+    raw = m.cpu().numpy()
+    doc = raw[:4 * n_tiles].view(np.int32)
+    bits_at = (4 * n_tiles + 255) // 256 * 256
+    bits = raw[bits_at:bits_at + 4 * n_tiles].view(np.uint32)
+    want_doc, want_bits = _doc_map_reference(off)
+    assert np.array_equal(doc, want_doc)
+    assert np.array_equal(bits, want_bits)
+
+
+@pytest.mark.parametrize("b", [1, 8, 17, 64])
+@pytest.mark.parametrize("lay", ["rows", "tiled"])
+def test_route_with_a_prebuilt_doc_map_is_identical(b, lay):
+    """Routing with the document map built once by msa_doc_map gives the
+    results of routing that builds it per call, bit for bit (narrow and
+    wide scans, both bank layouts), over repeated calls and fresh queries."""
+    g = torch.Generator().manual_seed(500 + b)
+    rows = torch.randint(1, 40, (600,), generator=g).numpy()
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    n_pool = int(off[-1])
+    kr = _randn(g, n_pool, 8, 128, dtype=torch.bfloat16).to(DEV)
+    bank = synth.tile_router_bank(kr) if lay == "tiled" else kr
+    offd = _dev(off)
+    m = msa.doc_map(offd, n_pool)
+    _say(f"route with a prebuilt document map: B={b}, {lay} bank, {n_pool} rows")
+    for rep in range(2):
+        qr = _randn(g, b, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+        i0, s0, d0 = msa.route(qr, bank, offd, 16, kr_layout=lay, n_pool=n_pool)
+        i1, s1, d1 = msa.route(qr, bank, offd, 16, kr_layout=lay, n_pool=n_pool, doc_map=m)
+        torch.cuda.synchronize()
+        assert torch.equal(d0.view(torch.int32), d1.view(torch.int32)), f"rep {rep}: document scores differ"
+        assert torch.equal(i0, i1) and torch.equal(s0.view(torch.int32), s1.view(torch.int32))
+    ref = oracle.doc_scores(np64(qr), np64(kr), off)
+    check_scores(np64(d1), ref, "prebuilt doc map")
+    check_topk(np64(i1), ref, 16, "prebuilt doc map")
+
+
 def test_route_top_k_bound_when_block_maxima_tie():
     """250,000 one-row documents (977 blocks of 256): 300 blocks share one
     tied maximum and the 16 blocks above it all sit in the same lane of the
