@@ -61,6 +61,12 @@ constexpr int kAMaxSplit = 4096;
 #ifndef MSA_ATT_PREROT      // 1: rotate local keys once when several query tiles read them
 #define MSA_ATT_PREROT 1
 #endif
+#ifndef MSA_ATT_WAVES_PER_CU   // work items (waves) per CU the key splits aim for
+#define MSA_ATT_WAVES_PER_CU 16
+#endif
+#ifndef MSA_ATT_BLOCK       // 1: prefill (>= 4 query tiles per KV head) shares key groups across a workgroup
+#define MSA_ATT_BLOCK 1
+#endif
 #ifndef MSA_ATT_MERGE_WAVE  // 1: merge with one wave per output row when there are at most 64 splits
 #define MSA_ATT_MERGE_WAVE 1
 #endif
@@ -412,6 +418,236 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
   }
 }
 
+// Block form for launches with at least four 16-row query tiles per KV head
+// (prefill): the four waves of a workgroup take four consecutive tiles of
+// one (query, KV head, key split) and share every 16-key group, which the
+// workgroup stages once in LDS - K row-major in padded rows (a wave's
+// A-operand reads of 16 rows hit 64 distinct banks), V transposed - double
+// buffered, one barrier per group.  Each thread loads one 16-byte piece of K
+// and four 4-byte pieces of V per group, so a group costs a workgroup what it
+// cost each wave before, and V is transposed once instead of four times.
+// Local keys come rotated (rope_local_kernel); only the query is rotated
+// here.  Scores, masking, the online softmax and the partials are those of
+// attend_kernel, per wave, with the wave's own causal key range; a wave
+// whose tile lies past the last one loads and synchronises but stores
+// nothing.
+template <int D>
+__global__ __launch_bounds__(kAWaves * 64, 2) void attend_block_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
+    const uint16_t *__restrict__ local_k, const uint16_t *__restrict__ local_v,
+    const int32_t *__restrict__ local_len, const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc,
+    float *__restrict__ part_ml, int B, int Tq, int Hq, int Hkv, int mem_cap, int local_cap, int n_mt, int n_split,
+    int split_len, int rps, float scale_log2, double log2_theta) {
+  using C = AttnCfg<D>;
+  constexpr int KS = C::KS, HS = C::HS, NT = C::NT, VTS = C::VTS, HALF = D / 2;
+  constexpr int KRS = D + 8;                               // K row stride in LDS (bf16)
+  constexpr int KT = 16 * (D / 8);                         // threads loading K (one 16-byte piece each)
+  constexpr int VT = 4 * (D / 2);                          // threads loading V (4 keys x 2 dims each)
+  constexpr int NTH = kAWaves * 64;
+  __shared__ __align__(16) uint16_t ks[2][16 * KRS];
+  __shared__ __align__(16) uint16_t vt[2][D * VTS];
+  __shared__ double omega[HALF];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // work item of the workgroup: (query, 4-tile group, split) of KV head g
+  const int n_mt4 = (n_mt + 3) / 4;
+  const int g = (int)(blockIdx.x % Hkv);
+  int64_t r = (int64_t)(blockIdx.x / Hkv);
+  if (r >= (int64_t)B * n_mt4 * n_split) return;          // the whole workgroup: no barrier is left waiting
+  const int split_i = (int)(r % n_split);
+  r /= n_split;
+  const int mt4 = (int)(r % n_mt4);
+  const int b = (int)(r / n_mt4);
+#if MSA_ATT_ROTATE
+  const int split = (int)((split_i + 5LL * b) % n_split);
+#else
+  const int split = split_i;
+#endif
+  const int mt = 4 * mt4 + wave;
+  const bool tile_ok = mt < n_mt;
+  const int G = Hq / Hkv;
+  const int M = max(0, min(mem_len[b], mem_cap));
+  const int T = max(0, min(local_len[b], local_cap));
+  const int o = pos_offset[b];
+  const int n_rows = Tq * G;
+  const int col = lane & 15, grp = lane >> 4;
+  const int R = mt * 16 + col;
+  const bool row_ok = tile_ok && R < n_rows;
+  const int t_row = row_ok ? R / G : 0;
+  const int i_row = T - Tq + t_row;
+  const int i_first = T - Tq + (mt * 16) / G;
+  // keys a tile sees: the memory, then local tokens up to its last token
+  auto key_end_of = [&](int tile) {
+    const int t_last = min(Tq - 1, (tile * 16 + 15) / G);
+    return M + max(0, min(T, T - Tq + t_last + 1));
+  };
+  const int k_begin = split * split_len;
+  const int k_end_g = min(key_end_of(min(4 * mt4 + 3, n_mt - 1)), k_begin + split_len);   // the workgroup's
+  const int k_end = tile_ok ? min(key_end_of(mt), k_begin + split_len) : k_begin;        // this wave's
+  const int64_t slot = (((int64_t)b * Hkv + g) * n_mt + mt) * n_split + split;
+
+  if (tid < HALF) omega[tid] = exp2(-(2.0 * tid / D) * log2_theta);
+  u32x4 qraw[KS];
+  {
+    const uint16_t *src = q + (((int64_t)b * Tq + t_row) * Hq + g * G + (row_ok ? R % G : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qraw[s] = ld16(src + 32 * s);
+  }
+
+  // cooperative loads of the 16-key group at kb (keys past the workgroup's
+  // range read its last key; every wave masks them)
+  const uint32_t mrow = 2u * Hkv * D, lrow = (uint32_t)Hkv * D;
+  auto key_k = [&](int k) -> const uint16_t * {
+    return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mrow + (int64_t)g * D
+                 : local_k + ((int64_t)b * local_cap + (k - M)) * lrow + (int64_t)g * D;
+  };
+  auto key_v = [&](int k) -> const uint16_t * {
+    return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mrow + lrow + (int64_t)g * D
+                 : local_v + ((int64_t)b * local_cap + (k - M)) * lrow + (int64_t)g * D;
+  };
+  const int kk = tid / (D / 8), ch = tid % (D / 8);        // K: key, 16-byte piece
+  const int qd = tid / (D / 2), dp = tid % (D / 2);        // V: key quad, dim pair
+  u32x4 kreg = {0u, 0u, 0u, 0u};
+  uint32_t vreg[4] = {0u, 0u, 0u, 0u};
+  auto gload = [&](int kb) {
+    if (KT >= NTH || tid < KT) kreg = ld16(key_k(min(kb + kk, k_end_g - 1)) + 8 * ch);
+    if (VT >= NTH || tid < VT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vreg[i] = *reinterpret_cast<const uint32_t *>(key_v(min(kb + 4 * qd + i, k_end_g - 1)) + 2 * dp);
+    }
+  };
+  auto lstore = [&](int buf) {
+    if (KT >= NTH || tid < KT) st16(&ks[buf][kk * KRS + 8 * ch], kreg);
+    if (VT >= NTH || tid < VT) {
+      u32x2 lo, hi;                                        // dims 2dp and 2dp+1 of keys 4qd .. 4qd+3
+      lo.x = (vreg[0] & 0xffffu) | (vreg[1] << 16);
+      lo.y = (vreg[2] & 0xffffu) | (vreg[3] << 16);
+      hi.x = (vreg[0] >> 16) | (vreg[1] & 0xffff0000u);
+      hi.y = (vreg[2] >> 16) | (vreg[3] & 0xffff0000u);
+      *reinterpret_cast<u32x2 *>(&vt[buf][(2 * dp) * VTS + 4 * qd]) = lo;
+      *reinterpret_cast<u32x2 *>(&vt[buf][(2 * dp + 1) * VTS + 4 * qd]) = hi;
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (k_begin < k_end_g) {                                 // (uniform over the workgroup)
+    gload(k_begin);
+    lstore(0);
+    __syncthreads();                                       // the first group and omega
+    // rotated, scaled query as B-operand fragments (hi + lo bf16)
+    u32x4 qhi[KS], qlo[KS];
+    {
+      float x[KS][8];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float f[8];
+        Elt<uint16_t>::unpack(qraw[s], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[s][e] = row_ok ? f[e] : 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < HS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float c, sn;
+          rope_phasor((double)o + (double)i_row, omega[32 * s + 8 * grp + e], &c, &sn);
+          const float x1 = x[s][e], x2 = x[s + HS][e];
+          x[s][e] = (x1 * c - x2 * sn) * scale_log2;
+          x[s + HS][e] = (x2 * c + x1 * sn) * scale_log2;
+        }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = bf16_to_f32(f32_to_bf16(x[s][e]));
+          lo[e] = x[s][e] - hi[e];
+        }
+        qhi[s] = Elt<uint16_t>::pack(hi);
+        qlo[s] = Elt<uint16_t>::pack(lo);
+      }
+    }
+    int buf = 0;
+    for (int kb = k_begin; kb < k_end_g; kb += 16) {
+      const bool more = kb + 16 < k_end_g;                 // (uniform)
+      if (more) gload(kb + 16);
+      // S^T = K Q^T: lane l holds S[row l%16][keys 4(l/16) .. +4]
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kv8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                                          &ks[buf][col * KRS + 32 * s + 8 * grp]));
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qhi[s]), sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qlo[s]), sc, 0, 0, 0);
+      }
+      if (!(kb + 15 < k_end && kb + 15 - M <= i_first)) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key = kb + 4 * grp + rr;
+          const bool ok = row_ok && key < k_end && (key < M || key - M <= i_row);
+          sc[rr] = ok ? sc[rr] : -INFINITY;
+        }
+      }
+      float mt_ = amax4(sc);
+      mt_ = fmaxf(mt_, __shfl_xor(mt_, 16, 64));
+      mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, 64));
+      const float m_new = fmaxf(m_run, mt_);
+      const bool none = m_new == -INFINITY;
+      const float corr = none ? 1.f : exp2f(m_run - m_new);
+      float psum = 0.f;
+      s16x4 pa;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float pr = none ? 0.f : exp2f(sc[rr] - m_new);
+        psum += pr;
+        pa[rr] = (short)f32_to_bf16(pr);
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * corr + psum;
+      if (__any(m_new > m_run)) {
+        float cr[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) cr[rr] = __shfl(corr, 4 * grp + rr, 64);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc[nt][rr] *= cr[rr];
+      }
+      m_run = m_new;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const u32x2 vb = *reinterpret_cast<const u32x2 *>(&vt[buf][(16 * nt + col) * VTS + 4 * grp]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, vb), acc[nt], 0, 0, 0);
+      }
+      if (more) lstore(buf ^ 1);
+      __syncthreads();                                     // next group in place; this one free
+      buf ^= 1;
+    }
+  }
+  if (!tile_ok) return;
+
+  // ---- partials: (m, l) from the S layout, acc from the O layout ----
+  if (grp == 0 && col < rps && row_ok) {
+    part_ml[2 * (slot * rps + col)] = m_run;
+    part_ml[2 * (slot * rps + col) + 1] = l_run;
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = 4 * grp + rr;
+    if (row < rps && mt * 16 + row < n_rows) {
+      float *dst = part_acc + (slot * rps + row) * D + col;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[nt][rr];
+    }
+  }
+}
+
 // Local keys rotated once to their positions o + i (i < local_len), for
 // launches in which several query tiles per KV head read every key: thread
 // per (query, token, KV head, 8 pairs), the phasor of each pair evaluated
@@ -594,7 +830,7 @@ void attend_plan(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32
   p->rps = std::min(16, q_tokens * G);
   const int64_t total = std::max<int64_t>(1, (int64_t)mem_cap + local_cap);
   const int64_t tiles = (int64_t)batch * hkv * p->n_mt;
-  const int64_t want = (int64_t)device_info().n_cu * 16;
+  const int64_t want = (int64_t)device_info().n_cu * MSA_ATT_WAVES_PER_CU;
   int64_t len = (total * tiles + want - 1) / want;
   len = std::max<int64_t>(64, std::min<int64_t>(MSA_ATT_SPLIT_MAX, ((len + 63) / 64) * 64));
   int64_t ns = (total + len - 1) / len;
@@ -645,6 +881,17 @@ static hipError_t launch_attend_t(const msa_attend_args &a, const AttendWs &ws, 
     if ((e = hipGetLastError()) != hipSuccess) return e;
     lk = ws.rot_k;
   }
+  if (PREROT && MSA_ATT_BLOCK && p.n_mt >= 4) {
+    const int64_t n_wg = (int64_t)a.n_kv_heads * a.batch * ((p.n_mt + 3) / 4) * p.n_split;
+    if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL((attend_block_kernel<D>), dim3((unsigned)n_wg), dim3(kAWaves * 64), 0, s,
+                          prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
+                          reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
+                          a.mem_len, lk, reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset,
+                          ws.part_acc, ws.part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap,
+                          a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e,
+                          log2(a.rope_theta));
+  } else
   hipExtLaunchKernelGGL((attend_kernel<D, PREROT>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
                         prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
                         reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
