@@ -643,7 +643,7 @@ def workload_prefill(args, dev):
          "routing": {"kernel": f"scan_wide_kernel<8, 4, 4> ({args.kr_layout} bank)", "bound": "mfma", "scan_us": float(scan_ms * 1e3),
                      "achieved_TFs": tfs, "peak_TFs": 2500.0, "frac": tfs / 2500.0, "bank": "MALL-warm (44.6 MB)",
                      "route_us": float(np.mean([route_ev.ms(i) for i in range(reps)]) * 1e3)},
-         "prefill_attention": {"kernel": "attend_block_kernel<128> (256 tokens, causal, GQA 32/8; four query tiles per workgroup share each key group)", "bound": "mfma",
+         "prefill_attention": {"kernel": "attend_block_kernel<128, 16> (256 tokens, causal, GQA 32/8; 16 query tiles per workgroup share each key group)", "bound": "mfma",
                                "memory_rows": mrows, "attend_us": float(att_ms * 1e3),
                                "achieved_TFs": att_flops / (att_ms / 1e3) / 1e12,
                                "with_merge_us": float(np.mean([pre_ev.ms(i) for i in range(reps)]) * 1e3)},

@@ -419,9 +419,9 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
 }
 
 // Block form for launches with at least four 16-row query tiles per KV head
-// (prefill): the four waves of a workgroup take four consecutive tiles of
-// one (query, KV head, key split) and share every 16-key group, which the
-// workgroup stages once in LDS - K row-major in padded rows (a wave's
+// (prefill): the NW waves of a workgroup (4, 8 or 16, as many as there are
+// tiles) take NW consecutive tiles of one (query, KV head, key split) and
+// share every 16-key group, which the workgroup stages once in LDS - K row-major in padded rows (a wave's
 // A-operand reads of 16 rows hit 64 distinct banks), V transposed - double
 // buffered, one barrier per group.  Each thread loads one 16-byte piece of K
 // and four 4-byte pieces of V per group, so a group costs a workgroup what it
@@ -431,8 +431,8 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
 // attend_kernel, per wave, with the wave's own causal key range; a wave
 // whose tile lies past the last one loads and synchronises but stores
 // nothing.
-template <int D>
-__global__ __launch_bounds__(kAWaves * 64, 2) void attend_block_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 8 / NW) void attend_block_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
     const uint16_t *__restrict__ local_k, const uint16_t *__restrict__ local_v,
     const int32_t *__restrict__ local_len, const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc,
@@ -443,14 +443,15 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_block_kernel(
   constexpr int KRS = D + 8;                               // K row stride in LDS (bf16)
   constexpr int KT = 16 * (D / 8);                         // threads loading K (one 16-byte piece each)
   constexpr int VT = 4 * (D / 2);                          // threads loading V (4 keys x 2 dims each)
-  constexpr int NTH = kAWaves * 64;
+  constexpr int NTH = NW * 64;
+  static_assert(NTH >= KT && NTH >= VT, "every piece of a key group needs a loading thread");
   __shared__ __align__(16) uint16_t ks[2][16 * KRS];
   __shared__ __align__(16) uint16_t vt[2][D * VTS];
   __shared__ double omega[HALF];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // work item of the workgroup: (query, 4-tile group, split) of KV head g
-  const int n_mt4 = (n_mt + 3) / 4;
+  // work item of the workgroup: (query, NW-tile group, split) of KV head g
+  const int n_mt4 = (n_mt + NW - 1) / NW;
   const int g = (int)(blockIdx.x % Hkv);
   int64_t r = (int64_t)(blockIdx.x / Hkv);
   if (r >= (int64_t)B * n_mt4 * n_split) return;          // the whole workgroup: no barrier is left waiting
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_block_kernel(
 #else
   const int split = split_i;
 #endif
-  const int mt = 4 * mt4 + wave;
+  const int mt = NW * mt4 + wave;
   const bool tile_ok = mt < n_mt;
   const int G = Hq / Hkv;
   const int M = max(0, min(mem_len[b], mem_cap));
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_block_kernel(
     return M + max(0, min(T, T - Tq + t_last + 1));
   };
   const int k_begin = split * split_len;
-  const int k_end_g = min(key_end_of(min(4 * mt4 + 3, n_mt - 1)), k_begin + split_len);   // the workgroup's
+  const int k_end_g = min(key_end_of(min(NW * mt4 + NW - 1, n_mt - 1)), k_begin + split_len);   // the workgroup's
   const int k_end = tile_ok ? min(key_end_of(mt), k_begin + split_len) : k_begin;        // this wave's
   const int64_t slot = (((int64_t)b * Hkv + g) * n_mt + mt) * n_split + split;
 
@@ -862,6 +863,20 @@ size_t attend_ws_layout(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv
   return end;
 }
 
+template <int D, int NW>
+static hipError_t launch_block(const msa_attend_args &a, const AttendPlan &p, const AttendWs &ws, const uint16_t *lk,
+                               float scale, hipStream_t s) {
+  const int64_t n_wg = (int64_t)a.n_kv_heads * a.batch * ((p.n_mt + NW - 1) / NW) * p.n_split;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL((attend_block_kernel<D, NW>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
+                        prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
+                        reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
+                        a.mem_len, lk, reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset,
+                        ws.part_acc, ws.part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap,
+                        a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
+  return hipGetLastError();
+}
+
 template <int D, bool PREROT>
 static hipError_t launch_attend_t(const msa_attend_args &a, const AttendWs &ws, hipStream_t s) {
   AttendPlan p;
@@ -882,23 +897,20 @@ static hipError_t launch_attend_t(const msa_attend_args &a, const AttendWs &ws, 
     lk = ws.rot_k;
   }
   if (PREROT && MSA_ATT_BLOCK && p.n_mt >= 4) {
-    const int64_t n_wg = (int64_t)a.n_kv_heads * a.batch * ((p.n_mt + 3) / 4) * p.n_split;
-    if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL((attend_block_kernel<D>), dim3((unsigned)n_wg), dim3(kAWaves * 64), 0, s,
+    // as many query tiles per workgroup as there are, up to 16
+    e = p.n_mt >= 16 ? launch_block<D, 16>(a, p, ws, lk, scale, s)
+        : p.n_mt >= 8 ? launch_block<D, 8>(a, p, ws, lk, scale, s)
+                      : launch_block<D, 4>(a, p, ws, lk, scale, s);
+    if (e != hipSuccess) return e;
+  } else {
+    hipExtLaunchKernelGGL((attend_kernel<D, PREROT>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
                           prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
                           reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
                           a.mem_len, lk, reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset,
                           ws.part_acc, ws.part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap,
-                          a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e,
-                          log2(a.rope_theta));
-  } else
-  hipExtLaunchKernelGGL((attend_kernel<D, PREROT>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
-                        prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
-                        reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
-                        a.mem_len, lk, reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset,
-                        ws.part_acc, ws.part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap,
-                        a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+                          a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int64_t rows = (int64_t)a.batch * a.q_tokens * a.n_q_heads;
   if (MSA_ATT_MERGE_WAVE && p.n_split <= 64)
     hipLaunchKernelGGL((attend_merge_wave_kernel<D>), dim3((unsigned)((rows + kAWaves - 1) / kAWaves)),

@@ -759,7 +759,7 @@ def test_attend_interleave_batch_shape():
 
 
 @pytest.mark.parametrize("hq,hkv,d,tq", [(32, 8, 128, 5), (16, 2, 64, 7), (16, 1, 64, 3), (8, 8, 128, 20),
-                                         (4, 2, 64, 33), (32, 8, 128, 13), (32, 4, 128, 9)])
+                                         (4, 2, 64, 33), (32, 8, 128, 13), (32, 4, 128, 9), (32, 8, 128, 40)])
 def test_attend_ragged_batch_and_head_shapes(hq, hkv, d, tq):
     """Ragged memory and local lengths (one query with fewer local tokens
     than query tokens, one without memory), groups of 1 to 16 query heads,
