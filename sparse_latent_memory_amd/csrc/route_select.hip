@@ -43,6 +43,7 @@ constexpr int kSortCap = kMaxTopK;           // keys the final selection can ord
 constexpr int kFastTopK = 64;                // k up to this uses the block-maximum bound
 constexpr int kBallotLists = 16;             // block maxima per lane in the ballot threshold (<= 1024 blocks)
 constexpr int kNarrow = 128;                 // block maxima at or above the lane bound searched in two lists
+constexpr int kSmallDocs = 4096;             // banks up to this many documents: every key in registers
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 #pragma unroll
@@ -100,6 +101,22 @@ __device__ __forceinline__ void for_doc_keys(const float *ds, int n_docs, F f) {
     for (int u = 0; u < 8; ++u)
       if (d0 + u * nt < n_docs) f(doc_key(v[u], d0 + u * nt));
   }
+}
+
+// The k-th largest of the wave's P*64 nonzero values v[] (0 where fewer
+// than k), bit by bit: the count of values >= a candidate is a sum of ballot
+// popcounts.
+template <int P>
+__device__ __forceinline__ uint32_t wave_kth_score(const uint32_t *v, int k) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < P; ++u) c += __popcll(__ballot(v[u] >= cand));
+    if (c >= k) t = cand;
+  }
+  return t;
 }
 
 __device__ __forceinline__ int64_t clamp_row(int64_t r, int64_t n_pool) {
@@ -263,7 +280,50 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
   const int len_in = plan && append ? mem_len[b] : 0;   // read early; written at the end
 
   bool sorted = false;
-  if (k <= kFastTopK && n_blocks <= kSortCap) {
+  if (k <= kFastTopK && n_docs <= kSmallDocs) {
+    // A small bank (the block bound is weak when there are fewer blocks than
+    // k): every document key stays in registers, thread t holding documents
+    // t, t + 256, ...  Each wave finds, bit by bit from ballot popcounts, the
+    // k-th largest score among its own documents; that wave holds k
+    // documents scoring at least that much, so the largest of the four wave
+    // values, L, bounds the k-th largest score overall from below, and the
+    // documents scoring >= L - k from the best wave and at most k (plus
+    // ties) from each other one - hold every winner.  One barrier shares the
+    // four values; the survivors are ranked below.
+    __shared__ uint32_t s_wl[kWaves];
+    constexpr int PER = kSmallDocs / kDocsPerBlock;
+    const int n_per = (n_docs + kDocsPerBlock - 1) / kDocsPerBlock;   // keys a thread holds, at most PER
+    uint64_t x[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int d = tid + u * kDocsPerBlock;
+      const float v = ds[min(d, n_docs - 1)];              // unconditional: a guarded load is waited for at once
+      x[u] = d < n_docs ? doc_key(v, d) : 0ull;
+    }
+    if (tid == 0) s_count = 0;
+    // score halves of the keys, 0 for slots past the last document (a
+    // candidate is never 0, so those never count); the search over 8 or 16
+    // slots is chosen once, with no branch inside it
+    uint32_t sk[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) sk[u] = (uint32_t)(x[u] >> 32);
+    const uint32_t wl = n_per <= PER / 2 ? wave_kth_score<PER / 2>(sk, k) : wave_kth_score<PER>(sk, k);
+    if ((tid & 63) == 0) s_wl[wave] = wl;
+    __syncthreads();
+    uint32_t L = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) L = max(L, s_wl[w]);
+    const uint64_t thr = (uint64_t)L << 32;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if (tid + u * kDocsPerBlock < n_docs && x[u] >= thr) {
+        const int pos = atomicAdd(&s_count, 1);
+        if (pos < kSortCap) sel[pos] = x[u];
+      }
+    }
+    __syncthreads();
+    sorted = true;                                         // at most n_docs <= kSortCap survivors
+  } else if (k <= kFastTopK && n_blocks <= kSortCap) {
     if (n_blocks <= 64 * kBallotLists) {
       // Wave 0 finds the score half T of the bound: the k-th largest block
       // maximum (score bits only).  The blocks whose maximum scores >= T -
