@@ -212,7 +212,6 @@ __global__ __launch_bounds__(kDocsPerBlock) void doc_parts_kernel(
     const float *__restrict__ doc_part, const float *__restrict__ tile_cont, const int64_t *__restrict__ pool_off,
     float *__restrict__ doc_scores, uint64_t *__restrict__ blockmax, int n_docs, int64_t n_pool, int B,
     int qstride) {
-  __shared__ uint64_t red[kWaves];
   const int n_blocks = gridDim.x;
   const int q0 = blockIdx.y * QC;
   const int d = blockIdx.x * kDocsPerBlock + threadIdx.x;
@@ -242,13 +241,31 @@ __global__ __launch_bounds__(kDocsPerBlock) void doc_parts_kernel(
       }
     }
   }
+  // block maxima of all QC queries behind one barrier: per wave the best
+  // score (shuffles) and the lowest document holding it (ballot), then the
+  // max of the four waves' keys
+  __shared__ uint64_t wmax[kWaves][QC];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d0 = blockIdx.x * kDocsPerBlock + wave * 64;  // document of lane 0
 #pragma unroll
   for (int i = 0; i < QC; ++i) {
     const int b = q0 + i;
     if (b >= B) break;                   // (uniform)
     if (valid) doc_scores[(int64_t)b * n_docs + d] = sc[i];
-    const uint64_t m = block_max_key(valid ? doc_key(sc[i], d) : 0, red);
-    if (threadIdx.x == 0) blockmax[(int64_t)b * n_blocks + blockIdx.x] = m;
+    const float v = valid ? sc[i] : -INFINITY;
+    float m = v;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    // keys order scores by their key bits, so compare those (-0 == +0 there)
+    const uint64_t hit = __ballot(valid && score_key(v) == score_key(m));
+    if (lane == 0) wmax[wave][i] = hit ? doc_key(m, d0 + __ffsll((unsigned long long)hit) - 1) : 0ull;
+  }
+  __syncthreads();
+  if (threadIdx.x < QC && q0 + (int)threadIdx.x < B) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) best = wmax[w][threadIdx.x] > best ? wmax[w][threadIdx.x] : best;
+    blockmax[(int64_t)(q0 + threadIdx.x) * n_blocks + blockIdx.x] = best;
   }
 }
 
