@@ -18,7 +18,7 @@ titles [HL], [TM], [GF]):
    query's start position offset by k, the number of retrieved documents,
    keeping the order background -> query -> generation ([HL]; [TM] stage 3).
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
 
 * R1 chunk = P consecutive tokens of one document; a tail chunk of n < P
   tokens is the plain mean of those n tokens; chunks never cross documents.
