@@ -46,7 +46,6 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 constexpr int kAWaves = 4;          // independent work items per workgroup
 constexpr int kAMaxSplit = 4096;
-constexpr int kAOnceSplit = 128;     // most splits of the one-pass merge
 #ifndef MSA_ATT_SPLIT_MAX   // longest key split, a multiple of 64
 #define MSA_ATT_SPLIT_MAX 512
 #endif
@@ -70,9 +69,6 @@ constexpr int kAOnceSplit = 128;     // most splits of the one-pass merge
 #endif
 #ifndef MSA_ATT_MERGE_WAVE  // 1: merge with one wave per output row when there are at most 64 splits
 #define MSA_ATT_MERGE_WAVE 1
-#endif
-#ifndef MSA_ATT_MERGE_ONCE  // 1: few output rows merge with all their loads issued at once (up to kAOnceSplit splits)
-#define MSA_ATT_MERGE_ONCE 1
 #endif
 #ifndef MSA_ATT_ROTATE      // 1: rotate each query's split order by its index
 #define MSA_ATT_ROTATE 1
@@ -823,77 +819,6 @@ __global__ __launch_bounds__(kAWaves * 64) void attend_merge_wave_kernel(
   if (lse && lane == 0) lse[bth] = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
-// The same combination for few output rows (a decode step of one or a few
-// queries), where the merge is bound by memory latency rather than by
-// bandwidth: every thread issues the loads of all its splits (m, l and its
-// float4 of the partial row) at once, clamped to the last split so that no
-// load sits under a branch; the maximum, the weights and the weighted sums
-// follow behind two barriers.  Thread (v, gq) owns float4 v of the row and
-// splits gq, gq + NGRP, ... as in attend_merge_kernel, and sums them in the
-// same order.
-template <int D>
-__global__ __launch_bounds__(256) void attend_merge_once_kernel(const float *__restrict__ part_acc,
-                                                               const float *__restrict__ part_ml,
-                                                               uint16_t *__restrict__ out, float *__restrict__ lse,
-                                                               int Tq, int Hq, int Hkv, int n_mt, int n_split,
-                                                               int rps) {
-  constexpr int NV = D / 4;               // float4 per output row
-  constexpr int NGRP = 256 / NV;          // split groups
-  constexpr int NU = kAOnceSplit / NGRP;  // splits per thread
-  __shared__ float s_m[4];
-  __shared__ float s_l[NGRP];
-  __shared__ float4 part[NGRP][NV];
-  const int64_t bth = blockIdx.x;                          // (b * Tq + t) * Hq + h
-  const int h = (int)(bth % Hq);
-  const int t = (int)((bth / Hq) % Tq);
-  const int b = (int)(bth / ((int64_t)Hq * Tq));
-  const int G = Hq / Hkv, g = h / G;
-  const int R = t * G + (h % G);
-  const int mt = R / 16, row = R % 16;
-  const int64_t base = ((((int64_t)b * Hkv + g) * n_mt + mt) * n_split) * rps + row;   // split s: base + s * rps
-  const int tid = threadIdx.x, v = tid % NV, gq = tid / NV;
-  float4 x[NU];
-  float2 ml[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int64_t i = base + (int64_t)min(gq + u * NGRP, n_split - 1) * rps;
-    x[u] = reinterpret_cast<const float4 *>(part_acc + i * D)[v];
-    ml[u] = *reinterpret_cast<const float2 *>(part_ml + 2 * i);
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) m = gq + u * NGRP < n_split ? fmaxf(m, ml[u].x) : m;
-  m = wave_max(m);
-  if ((tid & 63) == 0) s_m[tid >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-  float4 a = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const bool use = gq + u * NGRP < n_split && ml[u].x != -INFINITY;
-    const float ws = use ? exp2f(ml[u].x - m) : 0.f;
-    a.x += ws * x[u].x; a.y += ws * x[u].y; a.z += ws * x[u].z; a.w += ws * x[u].w;
-    l += ws * ml[u].y;
-  }
-  part[gq][v] = a;
-  if (v == 0) s_l[gq] = l;
-  __syncthreads();
-  if (tid < NV) {
-    float4 r = {0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
-#pragma unroll
-    for (int q2 = 0; q2 < NGRP; ++q2) {
-      r.x += part[q2][tid].x; r.y += part[q2][tid].y; r.z += part[q2][tid].z; r.w += part[q2][tid].w;
-      L += s_l[q2];
-    }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    uint16_t *o = out + bth * D + 4 * tid;
-    *reinterpret_cast<uint2 *>(o) = make_uint2(pack_bf16x2(r.x * inv, r.y * inv), pack_bf16x2(r.z * inv, r.w * inv));
-    if (lse && tid == 0) lse[bth] = L > 0.f ? (m + log2f(L)) * 0.69314718055994531f : -INFINITY;
-  }
-}
-
 }  // namespace
 
 // Keys per split: enough work items (waves) to give every CU about 16, in
@@ -987,11 +912,7 @@ static hipError_t launch_attend_t(const msa_attend_args &a, const AttendWs &ws, 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t rows = (int64_t)a.batch * a.q_tokens * a.n_q_heads;
-  if (MSA_ATT_MERGE_ONCE && p.n_split <= kAOnceSplit && rows <= device_info().n_cu)
-    hipLaunchKernelGGL((attend_merge_once_kernel<D>), dim3((unsigned)rows), dim3(256), 0, s, ws.part_acc, ws.part_ml,
-                       reinterpret_cast<uint16_t *>(a.out), a.lse, a.q_tokens, a.n_q_heads, a.n_kv_heads, p.n_mt,
-                       p.n_split, p.rps);
-  else if (MSA_ATT_MERGE_WAVE && p.n_split <= 64)
+  if (MSA_ATT_MERGE_WAVE && p.n_split <= 64)
     hipLaunchKernelGGL((attend_merge_wave_kernel<D>), dim3((unsigned)((rows + kAWaves - 1) / kAWaves)),
                        dim3(kAWaves * 64), 0, s, ws.part_acc, ws.part_ml, reinterpret_cast<uint16_t *>(a.out), a.lse,
                        rows, a.q_tokens, a.n_q_heads, a.n_kv_heads, p.n_mt, p.n_split, p.rps);
