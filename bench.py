@@ -367,7 +367,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, kr, pool_off, qrs[W], args.cpu_seconds)
+        step_in = {"enc_bank": enc_bank, "enc_tok_off": synth.row_offsets(enc_lens, 1), "enc_pool": enc.pool,
+                   "rope_theta": cfg.rope_theta, "k": k, "q": qs[W], "mem_kv": asm.mem_kv, "mem_len": asm.mem_len,
+                   "local_k": lk, "local_v": lv, "local_len": loc_len, "pos": pos}
+        cpu = cpu_baseline(cfg, kr, pool_off, qrs[W], args.cpu_seconds, step_in)
 
     res = {
         "metric": "bank tokens scored/s (% HBM peak); p50 route+decode step at 100M bank",
@@ -494,7 +497,7 @@ def workload_interleave(args, dev):
     reps = args.reps
     scan_ev = HipEvents(reps * R)
     route_ev, dec_ev = StreamEvents(reps * R), StreamEvents(reps * R)
-    mem_rows = np.zeros((reps, R + 1), dtype=np.int64)
+    mem_len_log = torch.zeros((reps, R + 1, B), dtype=torch.int32, device=dev)   # read after the timed loop
 
     def one(rep, timed):
         for r in range(R):
@@ -511,7 +514,7 @@ def workload_interleave(args, dev):
                               dws, stream=stream)
             if timed:
                 dec_ev.pairs[i][1].record(stream)
-                mem_rows[rep, r + 1] = int(asm.mem_len.sum())   # synchronises: outside the timed events
+                mem_len_log[rep, r + 1].copy_(asm.mem_len)         # device copy: no host synchronisation
 
     for _ in range(2):
         one(0, False)
@@ -521,6 +524,7 @@ def workload_interleave(args, dev):
         one(rep, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    mem_rows = mem_len_log.to(torch.int64).sum(-1).cpu().numpy()
     scan = np.array([[scan_ev.elapsed_ms(rep * R + r) for r in range(R)] for rep in range(reps)])
     route = np.array([[route_ev.ms(rep * R + r) for r in range(R)] for rep in range(reps)])
     dec = np.array([[dec_ev.ms(rep * R + r) for r in range(R)] for rep in range(reps)])
@@ -768,12 +772,17 @@ WORKLOADS = {"bank-100M": None, "encode-100M": workload_encode, "interleave-50M"
              "needles-16M": workload_needles}
 
 
-def cpu_baseline(cfg, kr, pool_off, qr, seconds):
-    """The float64 CPU oracle's routing on a bounded sample of the same bank:
-    consecutive blocks of 2048 documents from the start of the bank, scored
-    until `seconds` of CPU time have passed, on one thread (its elementwise
-    NumPy work is single-threaded anyway; BLAS is held to one thread too).
-    The first block is also timed with every thread of the process allowed."""
+def cpu_baseline(cfg, kr, pool_off, qr, seconds, step_in=None):
+    """The float64 CPU oracle on a bounded sample of the same step, on one
+    thread (its elementwise NumPy work is single-threaded anyway; BLAS is
+    held to one thread too).  Routing: consecutive blocks of 2048 documents
+    from the start of the bank, scored until `seconds` of CPU time have
+    passed; the first block is also timed with every thread of the process
+    allowed.  With `step_in`, the rest of the step is timed once each: the
+    encode batch (oracle.pool), the top-k over the sampled scores, and the
+    decode step over the gathered memory and the local context; the
+    whole-step rate scales the scoring and the top-k from the sample to the
+    full bank (both are linear in the documents) and adds the other two."""
     import oracle
     from threadpoolctl import threadpool_limits
 
@@ -781,14 +790,37 @@ def cpu_baseline(cfg, kr, pool_off, qr, seconds):
     block = 2048
     done_docs, spent = 0, 0.0
     n_docs = len(pool_off) - 1
+    parts = []
     with threadpool_limits(limits=1):
         while spent < seconds and done_docs < n_docs:
             d0, d1 = done_docs, min(done_docs + block, n_docs)
             rows = kr[pool_off[d0]:pool_off[d1]].float().cpu().double().numpy()
             t = time.perf_counter()
-            oracle.doc_scores(qn, rows, pool_off[d0:d1 + 1] - pool_off[d0])
+            parts.append(oracle.doc_scores(qn, rows, pool_off[d0:d1 + 1] - pool_off[d0]))
             spent += time.perf_counter() - t
             done_docs = d1
+        step = None
+        if step_in is not None:
+            f64 = lambda x: x.detach().float().cpu().double().numpy()
+            i64 = lambda x: x.detach().cpu().numpy().astype(np.int64)
+            dsc = np.concatenate(parts, axis=1)
+            t = time.perf_counter()
+            oracle.topk(dsc, step_in["k"])
+            t_topk = time.perf_counter() - t
+            eb = step_in["enc_bank"]
+            ek, ev, ekr = f64(eb["k"]), f64(eb["v"]), f64(eb["kr"])
+            t = time.perf_counter()
+            oracle.pool(ek, ev, ekr, step_in["enc_tok_off"], step_in["enc_pool"], step_in["rope_theta"])
+            t_pool = time.perf_counter() - t
+            dq, dm, dlk, dlv = f64(step_in["q"]), f64(step_in["mem_kv"]), f64(step_in["local_k"]), f64(step_in["local_v"])
+            t = time.perf_counter()
+            oracle.decode(dq, dm, i64(step_in["mem_len"]), dlk, dlv, i64(step_in["local_len"]), i64(step_in["pos"]),
+                          step_in["rope_theta"])
+            t_dec = time.perf_counter() - t
+            scale = n_docs / done_docs
+            t_step = (spent + t_topk) * scale + t_pool + t_dec
+            step = {"step_s": t_step, "scoring_s": spent * scale, "topk_s": t_topk * scale, "encode_batch_s": t_pool,
+                    "decode_s": t_dec, "scoring_rate": done_docs * 512 * cfg.batch / spent}
     tokens = done_docs * 512
     allowed = len(os.sched_getaffinity(0))
     rows = kr[pool_off[0]:pool_off[block]].float().cpu().double().numpy()
@@ -801,11 +833,21 @@ def cpu_baseline(cfg, kr, pool_off, qr, seconds):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": tokens * cfg.batch / spent, "unit": "bank tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle.doc_scores (NumPy float64, one thread) over the first {done_docs} documents "
-                      f"({tokens} bank tokens, {int(pool_off[done_docs])} pooled rows) of the same bank, "
-                      f"one query token, in blocks of {block} documents; {spent:.1f} s of compute",
-            "all_threads_value": block * 512 * cfg.batch / t_all, "all_threads": allowed, "cpu_model": model}
+    res = {"value": tokens * cfg.batch / spent, "unit": "bank tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"oracle.doc_scores (NumPy float64, one thread) over the first {done_docs} documents "
+                     f"({tokens} bank tokens, {int(pool_off[done_docs])} pooled rows) of the same bank, "
+                     f"one query token, in blocks of {block} documents; {spent:.1f} s of compute",
+           "all_threads_value": block * 512 * cfg.batch / t_all, "all_threads": allowed, "cpu_model": model}
+    if step is not None:
+        res["value"] = n_docs * 512 * cfg.batch / step["step_s"]
+        res["sample"] = (f"the whole step's oracle (NumPy float64, one thread): oracle.doc_scores over the first "
+                         f"{done_docs} documents ({tokens} bank tokens, {int(pool_off[done_docs])} pooled rows) of "
+                         f"the same bank in blocks of {block} documents ({spent:.1f} s) and oracle.topk over their "
+                         f"scores, both scaled to all {n_docs} documents, plus oracle.pool of the 64-document encode "
+                         f"batch and oracle.decode of the step's query; value = bank tokens / that step time")
+        res["step_components_s"] = {k_: round(v_, 4) for k_, v_ in step.items() if k_.endswith("_s")}
+        res["scoring_only_value"] = step["scoring_rate"]
+    return res
 
 
 if __name__ == "__main__":
