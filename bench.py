@@ -823,9 +823,10 @@ def cpu_baseline(cfg, kr, pool_off, qr, seconds, step_in=None):
                     "decode_s": t_dec, "scoring_rate": done_docs * 512 * cfg.batch / spent}
     tokens = done_docs * 512
     allowed = len(os.sched_getaffinity(0))
-    rows = kr[pool_off[0]:pool_off[block]].float().cpu().double().numpy()
+    b_all = min(block, n_docs)
+    rows = kr[pool_off[0]:pool_off[b_all]].float().cpu().double().numpy()
     t = time.perf_counter()
-    oracle.doc_scores(qn, rows, pool_off[:block + 1])
+    oracle.doc_scores(qn, rows, pool_off[:b_all + 1])
     t_all = time.perf_counter() - t
     model = ""
     try:
@@ -837,7 +838,7 @@ def cpu_baseline(cfg, kr, pool_off, qr, seconds, step_in=None):
            "sample": f"oracle.doc_scores (NumPy float64, one thread) over the first {done_docs} documents "
                      f"({tokens} bank tokens, {int(pool_off[done_docs])} pooled rows) of the same bank, "
                      f"one query token, in blocks of {block} documents; {spent:.1f} s of compute",
-           "all_threads_value": block * 512 * cfg.batch / t_all, "all_threads": allowed, "cpu_model": model}
+           "all_threads_value": b_all * 512 * cfg.batch / t_all, "all_threads": allowed, "cpu_model": model}
     if step is not None:
         res["value"] = n_docs * 512 * cfg.batch / step["step_s"]
         res["sample"] = (f"the whole step's oracle (NumPy float64, one thread): oracle.doc_scores over the first "
