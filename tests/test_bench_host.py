@@ -40,3 +40,21 @@ def test_cpu_baseline_times_the_whole_step_oracle():
     assert np.isclose(r["value"], n_docs * 512 * cfg.batch / c["step_s"], rtol=2e-3)
     # the whole step is slower than its scoring alone
     assert r["value"] <= r["scoring_only_value"] * 1.001
+
+
+def test_scan_traffic_record_is_current_and_guarded(tmp_path, monkeypatch):
+    # the committed counter record was taken on the current scan sources
+    rec = bench.measured_traffic(bench.SCAN_KERNEL)
+    assert rec is not None and 1.0 <= rec / 3_200_010_240 < 1.05
+    # a record of other sources, or of another kernel, is not used
+    import json
+    with open(bench.TRAFFIC_RECORD) as f:
+        good = json.load(f)
+    stale = dict(good, source_sha256="0" * 64)
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(stale))
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(path))
+    assert bench.measured_traffic(bench.SCAN_KERNEL) is None
+    path.write_text(json.dumps(good))
+    assert bench.measured_traffic("some_other_kernel<1>") is None
+    assert bench.measured_traffic(bench.SCAN_KERNEL) == good["hbm_bytes_per_launch"]
