@@ -66,6 +66,39 @@ def test_rope_closed_form_single_pair():
         np.testing.assert_allclose(got, [math.cos(p), math.sin(p)], atol=1e-15)
 
 
+def test_rope_worked_example_exact_frequencies(golden_dir):
+    # theta chosen so that every frequency theta^(-2j/D) is a power of 1/4:
+    # pins the schedule's exponent and the rotate-half pairing for j >= 1
+    g = _load(golden_dir, "rope_worked_example.json")
+    assert len(g["cases"]) == 12
+    for c in g["cases"]:
+        x = np.array(c["x"], dtype=np.float64)[None, None, :]
+        got = oracle.rope(x, [c["pos"]], c["theta"])[0, 0]
+        np.testing.assert_allclose(got, c["rope"], rtol=0, atol=1e-15, err_msg=c["formula"])
+
+
+@pytest.mark.parametrize("head_dim,theta", [(128, 1e6), (64, 1e4)])
+def test_rope_matches_transformers_qwen3_rotary(head_dim, theta):
+    # an implementation written by others: the Qwen3 rotary embedding of the
+    # transformers library (rotate-half, theta^(-2j/D) in float32).  Its float32
+    # frequencies move an angle by at most p * 2^-24 * omega, so positions stay
+    # below 4096 and the bound is 1e-3 of each vector's norm; a wrong exponent
+    # or interleaved pairs give errors of order one.
+    tf = pytest.importorskip("transformers")
+    from transformers.models.qwen3 import modeling_qwen3 as q3
+    cfg = tf.Qwen3Config(head_dim=head_dim, rope_theta=theta, hidden_size=2 * head_dim, num_attention_heads=2,
+                         num_key_value_heads=1)
+    emb = q3.Qwen3RotaryEmbedding(cfg)
+    pos = torch.arange(0, 4096, 37)[None]
+    x = torch.from_numpy(RNG.standard_normal((1, 2, pos.shape[1], head_dim)))
+    cos, sin = emb(x, pos)
+    ref, _ = q3.apply_rotary_pos_emb(x, x, cos, sin)
+    got = np.stack([oracle.rope(x[0, h].numpy(), pos[0].numpy(), theta) for h in range(2)])
+    err = np.linalg.norm(got - ref[0].numpy(), axis=-1) / np.linalg.norm(got, axis=-1)
+    assert err.max() < 1e-3, err.max()
+    np.testing.assert_allclose(oracle.rope_inv_freq(head_dim, theta), emb.inv_freq.double().numpy(), rtol=2e-7)
+
+
 def test_rope_invariants():
     d = 64
     x = RNG.standard_normal((1, 1, d))
@@ -229,6 +262,19 @@ def test_scores_range_and_self_match():
     assert oracle.topk(dsc2, 1)[0][0, 0] == d
 
 
+def test_scores_norm_clamp_closed_form():
+    # cos(x, y) = <x,y> / (max(|x|, 1e-8) max(|y|, 1e-8)): a key c * q_hat scores
+    # c / 1e-8 below the clamp and exactly 1 above it, per head, so the head
+    # mean is the mean of those values
+    q = RNG.standard_normal((1, 1, 2, 8))
+    qhat = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    for c, want in [(1e-9, 0.1), (2.5e-9, 0.25), (1e-6, 1.0), (1e-3, 1.0)]:
+        kr = (c * qhat[0, 0])[None]                                   # one row, both heads scaled by c
+        np.testing.assert_allclose(oracle.doc_scores(q, kr, [0, 1]), [[want]], rtol=1e-9)
+    kr = np.stack([1e-9 * qhat[0, 0, 0], 5.0 * qhat[0, 0, 1]])[None]   # heads 0.1 and 1
+    np.testing.assert_allclose(oracle.doc_scores(q, kr, [0, 1]), [[0.55]], rtol=1e-9)
+
+
 def test_scores_invariances():
     kr, off = _bank(30, 5, 4, 8)
     qr = RNG.standard_normal((2, 3, 4, 8))
@@ -319,6 +365,12 @@ def test_assemble_copies_rows_in_rank_order_and_drops_overflow():
     # query 1: doc 4 has 9 rows, doc 1 fits (10), doc 0 overflows: dropped
     assert mlen[1] == 10 and taken[1] == 2
     assert np.array_equal(mem[1, :9], kv[11:20]) and np.array_equal(mem[1, 9], kv[3])
+    # a lower-ranked document that would still fit is dropped with the one
+    # that overflowed: docs 2 (5 rows) and 4 (9 rows) leave 1 row of 7 free
+    # after doc 2, doc 4 does not fit, doc 1 (1 row) would, but is not taken
+    mem3, mlen3, taken3 = oracle.assemble(kv, off, np.array([[2, 4, 1]]), mem_cap=7)
+    assert mlen3.tolist() == [5] and taken3.tolist() == [1]
+    assert not mem3[0, 5:].any()
     # appending after existing rows
     mem2, mlen2, _ = oracle.assemble(kv, off, idx[:, :1], mem_cap=12, start_len=[2, 0])
     assert mlen2.tolist() == [7, 9]
