@@ -268,8 +268,9 @@ int msa_doc_map(const int64_t *doc_pool_off, int32_t n_docs, int64_t n_pool, voi
  * M and T are clamped to [0, mem_cap] and [0, local_cap].  fp32 softmax and
  * accumulation; out is rounded to nearest-even into `dtype`.  bf16 runs
  * msa_sparse_attend's matrix-core kernel with one query token (same
- * arithmetic as described there) when q and out are 16-byte aligned; fp32,
- * or unaligned q/out, runs a split-KV kernel in fp32 vector arithmetic.
+ * arithmetic as described there) and needs q and out 16-byte aligned
+ * (MSA_ERR_INVALID_ARG otherwise); fp32 runs a split-KV kernel in fp32
+ * vector arithmetic.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int32_t dtype;            /* msa_dtype of q, mem_kv, local_k/v, out       */

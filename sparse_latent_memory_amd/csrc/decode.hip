@@ -367,9 +367,7 @@ size_t decode_ws_layout(int32_t batch, int32_t hq, int32_t d, int32_t mem_cap, i
 
 hipError_t launch_decode(const msa_decode_args &a, float *part_acc, float *part_ml, int32_t n_split,
                          hipStream_t s) {
-  if (a.dtype == MSA_BF16)
-    return a.head_dim == 128 ? launch_t<uint16_t, 128>(a, part_acc, part_ml, n_split, s)
-                             : launch_t<uint16_t, 64>(a, part_acc, part_ml, n_split, s);
+  if (a.dtype != MSA_F32) return hipErrorInvalidValue;   // bf16 runs the block-attention kernel
   return a.head_dim == 128 ? launch_t<float, 128>(a, part_acc, part_ml, n_split, s)
                            : launch_t<float, 64>(a, part_acc, part_ml, n_split, s);
 }

@@ -332,8 +332,10 @@ int msa_sparse_decode(const msa_decode_args *a, void *stream) {
   if ((a->mem_kv && !aligned16(a->mem_kv)) || (a->local_k && !aligned16(a->local_k)) ||
       (a->local_v && !aligned16(a->local_v)))
     return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: K/V tensors must be 16-byte aligned");
+  if (a->dtype == MSA_BF16 && (!aligned16(a->q) || !aligned16(a->out)))
+    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: bf16 q and out must be 16-byte aligned");
   float *part_acc = nullptr, *part_ml = nullptr;
-  if (a->dtype == MSA_BF16 && aligned16(a->q) && aligned16(a->out)) {
+  if (a->dtype == MSA_BF16) {
     // the block-attention kernel with one query token
     msa_attend_args t = {};
     t.dtype = a->dtype;

@@ -273,6 +273,9 @@ def _decode_args(**kw):
     ({"local_v": None}, _lib.MSA_ERR_INVALID_ARG),
     ({"rope_theta": -1.0}, _lib.MSA_ERR_INVALID_ARG),
     ({"local_k": ctypes.c_void_p(_B + 4)}, _lib.MSA_ERR_INVALID_ARG),
+    ({"q": ctypes.c_void_p(_B + 8)}, _lib.MSA_ERR_INVALID_ARG),   # bf16 query not 16-byte aligned
+    ({"out": ctypes.c_void_p(_B + 2)}, _lib.MSA_ERR_INVALID_ARG),  # bf16 output not 16-byte aligned
+    ({"dtype": 0, "q": ctypes.c_void_p(_B + 4)}, _lib.MSA_ERR_WORKSPACE),   # fp32 takes any 4-byte alignment
     ({}, _lib.MSA_ERR_WORKSPACE),
 ])
 def test_decode_rejects_bad_arguments(kw, code):
