@@ -308,6 +308,20 @@ int msa_sparse_decode(const msa_decode_args *args, void *stream);
 size_t msa_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                   int32_t mem_cap, int32_t local_cap);
 
+/* msa_sparse_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the split partials in
+ * a static device array of the library (64 MiB, one per device, held until
+ * the process ends) instead of a workspace.  args->workspace and
+ * args->workspace_bytes are ignored; the call allocates nothing.  A call
+ * whose partials exceed 64 MiB (msa_decode_workspace_bytes() > 64 MiB for
+ * its sizes) returns MSA_ERR_WORKSPACE and enqueues nothing.  Every call on
+ * one device uses the same array: calls whose execution overlaps on one
+ * device (different streams, no ordering between them) race and give wrong
+ * results; calls ordered on one stream are safe.  Other arguments,
+ * validation and errors as for msa_sparse_decode. */
+int msa_sparse_decode_noalloc(const msa_decode_args *args, void *stream);
+
 /* ------------------------------------------------------------------------
  * Stage 3 for a block of query tokens - prefill through the sparse context.
  *

@@ -21,8 +21,9 @@ from ._lib import (  # noqa: F401
     route_workspace_bytes,
     sparse_attend,
     sparse_decode,
+    sparse_decode_noalloc,
 )
 
 __all__ = ["Assembly", "MSAError", "attend_workspace_bytes", "bank_rows", "decode_workspace_bytes", "doc_map",
            "doc_map_bytes", "load", "pool_encode", "route", "route_workspace_bytes", "sparse_attend", "sparse_decode",
-           "synth"]
+           "sparse_decode_noalloc", "synth"]

@@ -79,7 +79,7 @@ class AttendArgs(ctypes.Structure):
 
 
 EXPORTS = ("msa_pool_encode", "msa_route", "msa_route_workspace_bytes", "msa_doc_map_bytes", "msa_doc_map",
-           "msa_sparse_decode",
+           "msa_sparse_decode", "msa_sparse_decode_noalloc",
            "msa_decode_workspace_bytes", "msa_sparse_attend", "msa_attend_workspace_bytes", "msa_last_error",
            "msa_version")
 
@@ -102,6 +102,8 @@ def load(path=None):
     lib.msa_route.restype = ctypes.c_int
     lib.msa_sparse_decode.argtypes = [ctypes.POINTER(DecodeArgs), P]
     lib.msa_sparse_decode.restype = ctypes.c_int
+    lib.msa_sparse_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), P]
+    lib.msa_sparse_decode_noalloc.restype = ctypes.c_int
     lib.msa_route_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I64, I32]
     lib.msa_route_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_doc_map_bytes.argtypes = [I64]
@@ -346,33 +348,52 @@ def decode_workspace_bytes(batch, n_q_heads, head_dim, mem_cap, local_cap):
     return int(load().msa_decode_workspace_bytes(batch, n_q_heads, head_dim, mem_cap, local_cap))
 
 
+def _decode_struct(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, rope_theta, out, lse,
+                   softmax_scale, want_lse, prof_events):
+    b, hq, d = q.shape
+    _, t_cap, hkv, _ = local_k.shape
+    m_cap = 0 if mem_kv is None else mem_kv.shape[1]
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=q.device)
+    a = DecodeArgs(dtype=dtype_code(q.dtype), batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, mem_cap=m_cap,
+                   local_cap=t_cap, q=_dptr(q, "q"), mem_kv=_dptr(mem_kv, "mem_kv"), mem_len=_dptr(mem_len, "mem_len"),
+                   local_k=_dptr(local_k, "local_k"), local_v=_dptr(local_v, "local_v"),
+                   local_len=_dptr(local_len, "local_len"), pos_offset=_dptr(pos_offset, "pos_offset"),
+                   rope_theta=float(rope_theta), softmax_scale=float(softmax_scale), out=_dptr(out, "out"),
+                   lse=_dptr(lse, "lse"))
+    if prof_events is not None:
+        a.prof_event_begin, a.prof_event_end = prof_events
+    return a, out, lse
+
+
 def sparse_decode(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, rope_theta,
                   out=None, lse=None, workspace=None, softmax_scale=0.0, want_lse=True, stream=None,
                   prof_events=None):
     """msa_sparse_decode.  q: [B, Hq, D]; mem_kv: [B, M_cap, 2, Hkv, D] (or
     None); local_k/v: [B, T_cap, Hkv, D]; mem_len, local_len, pos_offset:
     int32 device [B].  Returns (out, lse)."""
-    b, hq, d = q.shape
-    _, t_cap, hkv, _ = local_k.shape
-    m_cap = 0 if mem_kv is None else mem_kv.shape[1]
-    dev = q.device
-    if out is None:
-        out = torch.empty((b, hq, d), dtype=q.dtype, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty((b, hq), dtype=torch.float32, device=dev)
+    a, out, lse = _decode_struct(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, rope_theta, out, lse,
+                                 softmax_scale, want_lse, prof_events)
     if workspace is None:
-        nbytes = decode_workspace_bytes(b, hq, d, m_cap, t_cap)
-        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-    a = DecodeArgs(dtype=dtype_code(q.dtype), batch=b, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, mem_cap=m_cap,
-                   local_cap=t_cap, q=_dptr(q, "q"), mem_kv=_dptr(mem_kv, "mem_kv"), mem_len=_dptr(mem_len, "mem_len"),
-                   local_k=_dptr(local_k, "local_k"), local_v=_dptr(local_v, "local_v"),
-                   local_len=_dptr(local_len, "local_len"), pos_offset=_dptr(pos_offset, "pos_offset"),
-                   rope_theta=float(rope_theta), softmax_scale=float(softmax_scale), out=_dptr(out, "out"),
-                   lse=_dptr(lse, "lse"), workspace=_dptr(workspace, "workspace"),
-                   workspace_bytes=workspace.numel())
-    if prof_events is not None:
-        a.prof_event_begin, a.prof_event_end = prof_events
+        nbytes = decode_workspace_bytes(a.batch, a.n_q_heads, a.head_dim, a.mem_cap, a.local_cap)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    a.workspace = _dptr(workspace, "workspace")
+    a.workspace_bytes = workspace.numel()
     _check(load().msa_sparse_decode(ctypes.byref(a), _stream(stream)))
+    return out, lse
+
+
+def sparse_decode_noalloc(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, rope_theta, out, lse=None,
+                          softmax_scale=0.0, stream=None):
+    """msa_sparse_decode_noalloc: msa_sparse_decode with the library's static
+    scratch in place of a workspace.  The caller passes every output (out,
+    and lse or None), so nothing is allocated here either.  Returns
+    (out, lse)."""
+    a, out, lse = _decode_struct(q, mem_kv, mem_len, local_k, local_v, local_len, pos_offset, rope_theta, out, lse,
+                                 softmax_scale, False, None)
+    _check(load().msa_sparse_decode_noalloc(ctypes.byref(a), _stream(stream)))
     return out, lse
 
 

@@ -312,31 +312,85 @@ size_t msa_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head
   return need;
 }
 
-int msa_sparse_decode(const msa_decode_args *a, void *stream) {
-  if (!a) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: args is NULL");
-  if (!dtype_ok(a->dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: bad dtype %d", a->dtype);
+}  // extern "C"
+
+namespace {
+
+// Device scratch of msa_sparse_decode_noalloc: the split partials that
+// msa_sparse_decode keeps in the caller's workspace.  Every device the
+// library runs on holds its own copy for the life of the process; calls on
+// one device share it.
+constexpr size_t kDecodeScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per
+// device while that device is current.  In host code `scratch` names a host
+// stand-in, never the device array, so only this address reaches a kernel.
+hipError_t scratch_address(void **out) {
+  static void *addr[64];
+  static hipError_t err[64];
+  static std::once_flag once[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    err[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch));
+    if (err[dev] == hipSuccess && !addr[dev]) err[dev] = hipErrorInvalidSymbol;
+  });
+  if (err[dev] != hipSuccess) return err[dev];
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// Shared body of msa_sparse_decode and msa_sparse_decode_noalloc: `ws` holds
+// `ws_bytes` bytes for the split partials (the caller's workspace, or the
+// static scratch when `noalloc`); `who` names the entry point in messages.
+int sparse_decode_with(const char *who, const msa_decode_args *a, void *ws, size_t ws_bytes, bool noalloc,
+                       void *stream) {
+  if (!a) return fail(MSA_ERR_INVALID_ARG, "%s: args is NULL", who);
+  if (!dtype_ok(a->dtype)) return fail(MSA_ERR_INVALID_ARG, "%s: bad dtype %d", who, a->dtype);
   if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1 || a->mem_cap < 0 || a->local_cap < 0 ||
       !(a->rope_theta > 0.0))
-    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: need batch, heads >= 1, caps >= 0, rope_theta > 0");
+    return fail(MSA_ERR_INVALID_ARG, "%s: need batch, heads >= 1, caps >= 0, rope_theta > 0", who);
   if (a->n_q_heads % a->n_kv_heads != 0)
-    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: n_q_heads (%d) not a multiple of n_kv_heads (%d)",
-                a->n_q_heads, a->n_kv_heads);
+    return fail(MSA_ERR_INVALID_ARG, "%s: n_q_heads (%d) not a multiple of n_kv_heads (%d)", who, a->n_q_heads,
+                a->n_kv_heads);
   if (a->n_q_heads / a->n_kv_heads > 8)
-    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_decode: more than 8 query heads per KV head");
-  if (!dim_ok(a->head_dim)) return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_decode: head_dim must be 64 or 128");
+    return fail(MSA_ERR_UNSUPPORTED, "%s: more than 8 query heads per KV head", who);
+  if (!dim_ok(a->head_dim)) return fail(MSA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", who);
   if ((int64_t)a->mem_cap + a->local_cap > (1LL << 30))
-    return fail(MSA_ERR_UNSUPPORTED, "msa_sparse_decode: context capacity too large");
+    return fail(MSA_ERR_UNSUPPORTED, "%s: context capacity too large", who);
   if (!a->q || !a->mem_len || !a->local_len || !a->pos_offset || !a->out || (a->mem_cap > 0 && !a->mem_kv) ||
       (a->local_cap > 0 && (!a->local_k || !a->local_v)))
-    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: NULL pointer");
+    return fail(MSA_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if ((a->mem_kv && !aligned16(a->mem_kv)) || (a->local_k && !aligned16(a->local_k)) ||
       (a->local_v && !aligned16(a->local_v)))
-    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: K/V tensors must be 16-byte aligned");
+    return fail(MSA_ERR_INVALID_ARG, "%s: K/V tensors must be 16-byte aligned", who);
   if (a->dtype == MSA_BF16 && (!aligned16(a->q) || !aligned16(a->out)))
-    return fail(MSA_ERR_INVALID_ARG, "msa_sparse_decode: bf16 q and out must be 16-byte aligned");
-  float *part_acc = nullptr, *part_ml = nullptr;
+    return fail(MSA_ERR_INVALID_ARG, "%s: bf16 q and out must be 16-byte aligned", who);
+  // bf16: the block-attention kernel with one query token; fp32: split-KV
+  size_t need = 0;
+  int32_t n_split = 0;
+  if (a->dtype == MSA_BF16)
+    need = attend_ws_layout(a->batch, 1, a->n_q_heads, a->n_kv_heads, a->head_dim, a->mem_cap, a->local_cap, nullptr,
+                            nullptr);
+  else
+    need = decode_ws_layout(a->batch, a->n_q_heads, a->head_dim, a->mem_cap, a->local_cap, nullptr, nullptr, nullptr,
+                            &n_split);
+  if (noalloc) {
+    if (need > kDecodeScratchBytes)
+      return fail(MSA_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch; the static scratch holds %zu", who,
+                  need, kDecodeScratchBytes);
+    const hipError_t se = scratch_address(&ws);
+    if (se != hipSuccess) return hip_fail(se, "msa_sparse_decode_noalloc: scratch address");
+    ws_bytes = kDecodeScratchBytes;
+  } else if (!ws || ws_bytes < need || !aligned16(ws)) {
+    return fail(MSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", who, need,
+                ws ? ws_bytes : (size_t)0);
+  }
+  hipError_t e = hipSuccess;
   if (a->dtype == MSA_BF16) {
-    // the block-attention kernel with one query token
     msa_attend_args t = {};
     t.dtype = a->dtype;
     t.batch = a->batch;
@@ -359,27 +413,30 @@ int msa_sparse_decode(const msa_decode_args *a, void *stream) {
     t.lse = a->lse;
     t.prof_event_begin = a->prof_event_begin;
     t.prof_event_end = a->prof_event_end;
-    const size_t need = attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap,
-                                         nullptr, nullptr);
-    if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
-      return fail(MSA_ERR_WORKSPACE, "msa_sparse_decode: workspace needs %zu bytes (16-byte aligned), got %zu",
-                  need, a->workspace ? a->workspace_bytes : (size_t)0);
     AttendWs aws;
-    attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap, a->workspace, &aws);
-    hipError_t e = launch_attend(t, aws, reinterpret_cast<hipStream_t>(stream));
-    return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_decode launch");
+    attend_ws_layout(t.batch, 1, t.n_q_heads, t.n_kv_heads, t.head_dim, t.mem_cap, t.local_cap, ws, &aws);
+    e = launch_attend(t, aws, reinterpret_cast<hipStream_t>(stream));
+  } else {
+    float *part_acc = nullptr, *part_ml = nullptr;
+    decode_ws_layout(a->batch, a->n_q_heads, a->head_dim, a->mem_cap, a->local_cap, ws, &part_acc, &part_ml,
+                     &n_split);
+    e = launch_decode(*a, part_acc, part_ml, n_split, reinterpret_cast<hipStream_t>(stream));
   }
-  int32_t n_split = 0;
-  const size_t need =
-      decode_ws_layout(a->batch, a->n_q_heads, a->head_dim, a->mem_cap, a->local_cap, nullptr, nullptr, nullptr,
-                       &n_split);
-  if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
-    return fail(MSA_ERR_WORKSPACE, "msa_sparse_decode: workspace needs %zu bytes (16-byte aligned), got %zu",
-                need, a->workspace ? a->workspace_bytes : (size_t)0);
-  decode_ws_layout(a->batch, a->n_q_heads, a->head_dim, a->mem_cap, a->local_cap, a->workspace, &part_acc,
-                   &part_ml, &n_split);
-  hipError_t e = launch_decode(*a, part_acc, part_ml, n_split, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_sparse_decode launch");
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "%s launch: %s (%d)", who, hipGetErrorString(e), (int)e);
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_sparse_decode(const msa_decode_args *a, void *stream) {
+  return sparse_decode_with("msa_sparse_decode", a, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0, false,
+                            stream);
+}
+
+int msa_sparse_decode_noalloc(const msa_decode_args *a, void *stream) {
+  return sparse_decode_with("msa_sparse_decode_noalloc", a, nullptr, 0, true, stream);
 }
 
 size_t msa_attend_workspace_bytes(int32_t batch, int32_t q_tokens, int32_t n_q_heads, int32_t n_kv_heads,

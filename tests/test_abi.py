@@ -284,6 +284,24 @@ def test_decode_rejects_bad_arguments(kw, code):
     assert lib.msa_sparse_decode(ctypes.byref(a), None) == code, lib.msa_last_error()
 
 
+@no_gpu
+def test_decode_noalloc_refuses_partials_beyond_its_static_scratch():
+    """msa_sparse_decode_noalloc keeps the split partials in a 64 MiB static
+    array: sizes that need more are refused before any launch (128 queries
+    of 32 heads over 16,384 keys need 65 MiB), and the caller's workspace
+    fields are ignored rather than used."""
+    lib = _lib.load()
+    assert lib.msa_decode_workspace_bytes(128, 32, 128, 12288, 4096) > (64 << 20)
+    a = _decode_args(batch=128, mem_cap=12288, local_cap=4096, workspace=None, workspace_bytes=0)
+    assert lib.msa_sparse_decode_noalloc(ctypes.byref(a), None) == _lib.MSA_ERR_WORKSPACE
+    assert b"static scratch" in lib.msa_last_error()
+    a = _decode_args(batch=128, mem_cap=12288, local_cap=4096, workspace=_p(), workspace_bytes=1 << 40)
+    assert lib.msa_sparse_decode_noalloc(ctypes.byref(a), None) == _lib.MSA_ERR_WORKSPACE
+    a = _decode_args(n_q_heads=30)
+    assert lib.msa_sparse_decode_noalloc(ctypes.byref(a), None) == _lib.MSA_ERR_INVALID_ARG
+    assert b"msa_sparse_decode_noalloc" in lib.msa_last_error()
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load(str(tmp_path / "missing" / "libmsa.so"))
