@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import sparse_latent_memory_amd as msa  # noqa: E402
+from sparse_latent_memory_amd.interleave import InterleavePipeline  # noqa: E402
 from sparse_latent_memory_amd import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E peak, GB/s
@@ -198,7 +199,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--latency-steps", type=int, default=50)
+    ap.add_argument("--latency-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--write-traffic-record", nargs=4,
@@ -352,6 +353,35 @@ def main():
         pipe_ms = (time.perf_counter() - t) * 1e3 / n_pipe
     log(f"route+decode pipelined interval {pipe_ms:.3f} ms")
 
+    # the same with the host-driven hipMemcpyAsync assembly: msa_route without
+    # assembly for query i, then msa_assemble (copy mode) for query i - 1,
+    # whose top-k has landed by then, so that query's copies cross the host
+    # link while query i is scored; msa_assemble blocks this thread only
+    # until query i - 1's ids are on the host
+    for L in lanes:
+        L["asm_c"] = msa.Assembly.allocate(host_kv, pool_off_h, cfg.batch, k, mem_cap, dev, mode="copies",
+                                           copy_stream=torch.cuda.Stream())
+
+    def finish(i, L):
+        msa.assemble(L["tki"], pool_off_d, L["asm_c"], stream=L["s"])
+        msa.sparse_decode(qs[i], L["asm_c"].mem_kv, L["asm_c"].mem_len, lk, lv, loc_len, pos, cfg.rope_theta,
+                          L["out"], L["lse"], L["dws"], stream=L["s"])
+
+    for rep in range(2):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        prev = None
+        for n, i in enumerate(range(W + K, n_steps)):
+            L = lanes[n % 2]
+            msa.route(qrs[i], bank, pool_off_d, k, L["dsc"], L["tki"], L["tks"], L["rws"], stream=L["s"], **rkw)
+            if prev is not None:
+                finish(*prev)
+            prev = (i, L)
+        finish(*prev)
+        torch.cuda.synchronize()
+        pipe_copy_ms = (time.perf_counter() - t) * 1e3 / n_pipe
+    log(f"route+decode pipelined interval, hipMemcpyAsync assembly {pipe_copy_ms:.3f} ms")
+
     scan_bytes = n_pool * cfg.n_router_heads * cfg.router_dim * 2 + cfg.n_router_heads * cfg.router_dim * 2
     scan_avg_s = scan_ms.mean() / 1e3
     achieved = scan_bytes / scan_avg_s / 1e9
@@ -416,6 +446,7 @@ def main():
             "route_decode_p99": float(np.percentile(lat["kernel"], 99)),
             "route_decode_p50_copy_gather": float(np.percentile(lat["copies"], 50)),
             "route_decode_pipelined_interval": float(pipe_ms),
+            "route_decode_pipelined_interval_copy_gather": float(pipe_copy_ms),
             "roofline_floor": float(t_floor_ms),
             "decode_attention_us": float(dec_ms.mean() * 1e3),
             "decode_achieved_GBs": float(dec_bytes / (dec_ms.mean() / 1e3) / 1e9),
@@ -545,15 +576,39 @@ def workload_interleave(args, dev):
             "decode_GBs": float(dec_bytes[r] / (dec[:, r].mean() / 1e3) / 1e9)})
     round_ms = (route + dec).mean()
     achieved = scan_bytes / (scan.mean() / 1e3) / 1e9
+
+    # ---- pipelined rounds (sparse_latent_memory_amd.interleave): round n's
+    # assembly crosses the host link while round n + 1 is scored and round
+    # n - 1 decoded; one group of R rounds per repetition, memory reset at
+    # each group's first round
+    pipe = InterleavePipeline(kr, off_d, rkw, host_kv, torch.as_tensor(off), B, k, mem_cap, lk, lv, loc_len,
+                              cfg.rope_theta, cfg.n_q_heads)
+
+    def pipelined(n_reps):
+        for _ in range(n_reps):
+            pipe.run(qrs, qs, pos)
+
+    torch.cuda.synchronize()
+    pipelined(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pipelined(reps)
+    torch.cuda.synchronize()
+    pipe_wall = time.perf_counter() - t0
+    pipe_round_ms = pipe_wall * 1e3 / (reps * R)
+    log(f"interleave: serial {round_ms:.3f} ms per round, pipelined {pipe_round_ms:.3f} ms per round")
     _supporting_line(
-        "query-rounds/s (route + gather + decode), memory interleave", B * R * reps / wall, "query-rounds/s",
+        "query-rounds/s (route + gather + decode), memory interleave", B * R * reps / pipe_wall, "query-rounds/s",
         f"interleave-50M: {n_docs} docs, {int(lens.sum())} tokens (lognormal, mean 1024), {n_pool} pooled rows; "
         f"64 queries x {R} rounds of top-{k}, memory <= {mem_cap} rows + {cfg.local_len} local tokens, "
         "GQA 32/8 x 128",
         {"kernel": f"route bank scan, 64 one-token queries (scan_wide_kernel<8, 4, 4>, {args.kr_layout} bank)", "bound": "hbm",
          "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
          "traffic": None},
-        {"ms_per_round": float(round_ms), "rounds": per_round, "reps": reps}, kr_layout=args.kr_layout)
+        {"ms_per_round": float(pipe_round_ms), "ms_per_round_serial": float(round_ms),
+         "schedule": "pipelined: round n's assembly overlaps round n+1's routing and round n-1's decode "
+                     "(three streams); the per-round figures below are from the serial schedule",
+         "rounds": per_round, "reps": reps}, kr_layout=args.kr_layout)
 
 
 def workload_prefill(args, dev):

@@ -233,6 +233,60 @@ size_t msa_route_workspace_bytes(int32_t dtype, int32_t batch, int32_t q_tokens,
                                  int32_t n_router_heads, int32_t router_dim,
                                  int32_t n_docs, int64_t n_pool, int32_t top_k);
 
+/* ------------------------------------------------------------------------
+ * Context assembly as a call of its own: the assembly part of msa_route
+ * for top-k ids it (or anything else) produced earlier.  Same sources and
+ * the same rule as msa_route's assembly: the documents topk_idx[b, 0..k)
+ * in rank order while they fit after the current length (append) or from
+ * row 0; an id outside [0, n_docs) ends query b's list.  mem_len[b] is the
+ * new length.
+ * Splitting routing from assembly lets the content of one routing round
+ * cross the host link while the next round is scored: call msa_route
+ * without assembly for round r+1 and msa_assemble for round r (the sources'
+ * "fetched when selected" tier, overlapped with scoring).
+ *  MSA_GATHER_KERNEL: a plan kernel and the gather kernel on `stream`, fully
+ *    asynchronous; host_kv device-mapped pinned memory; needs the
+ *    workspace (msa_assemble_workspace_bytes) and doc_pool_off on the device.
+ *  MSA_GATHER_COPIES: BLOCKS the calling thread until topk_idx (read on
+ *    `stream`, after the work already queued there) is in host_topk_idx,
+ *    then one hipMemcpyAsync per document on copy_stream; `stream` waits for
+ *    the copies.  Uses host_doc_pool_off; no workspace.  Any pinned host_kv.
+ * Errors as for msa_route's assembly arguments, plus batch >= 1,
+ * 1 <= top_k <= min(n_docs, 4096) and a NULL topk_idx.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch;                    /* B >= 1                               */
+  int32_t top_k;                    /* k ids per query                      */
+  int32_t n_docs;
+  int32_t kv_dtype;                 /* msa_dtype of host_kv and mem_kv      */
+  int64_t n_pool;                   /* = doc_pool_off[n_docs]               */
+  const int32_t *topk_idx;          /* device [B, k], rank order            */
+  const int64_t *doc_pool_off;      /* device [n_docs+1] (kernel mode)      */
+  const void *host_kv;              /* pinned host [n_pool, 2, Hkv, D]      */
+  const int64_t *host_doc_pool_off; /* host [n_docs+1] (copies mode)        */
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t mem_cap;                  /* rows per query in mem_kv             */
+  int32_t append;                   /* 1: append after the current length   */
+  int32_t gather_mode;              /* msa_gather_mode                      */
+  int32_t reserved0;
+  void *mem_kv;                     /* device [B, mem_cap, 2, Hkv, D]       */
+  int32_t *mem_len;                 /* device [B]: out; in when appending   */
+                                    /*   in MSA_GATHER_KERNEL mode          */
+  int32_t *host_topk_idx;           /* pinned host out [B, k]     (copies)  */
+  int32_t *host_mem_len;            /* pinned host in/out [B]     (copies)  */
+  int32_t *host_mem_docs;           /* pinned host out [B]; opt.  (copies)  */
+  void *copy_stream;                /* hipStream_t for the copies (copies)  */
+  void *workspace;                  /* device (kernel mode)                 */
+  size_t workspace_bytes;
+} msa_assemble_args;
+
+int msa_assemble(const msa_assemble_args *args, void *stream);
+
+/* Workspace for msa_assemble in the kernel mode (the copy plan), in bytes
+ * (0 on invalid sizes). */
+size_t msa_assemble_workspace_bytes(int32_t batch, int32_t top_k);
+
 /* Document map of a router bank: an optional input of msa_route.
  * The document path of msa_route (one token per query on the matrix-core
  * scans) reduces each 16-row tile of the bank per document inside the scan;

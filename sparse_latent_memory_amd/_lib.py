@@ -56,6 +56,16 @@ class RouteArgs(ctypes.Structure):
     ]
 
 
+class AssembleArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", I32), ("top_k", I32), ("n_docs", I32), ("kv_dtype", I32), ("n_pool", I64),
+        ("topk_idx", P), ("doc_pool_off", P), ("host_kv", P), ("host_doc_pool_off", P),
+        ("n_kv_heads", I32), ("head_dim", I32), ("mem_cap", I32), ("append", I32), ("gather_mode", I32),
+        ("reserved0", I32), ("mem_kv", P), ("mem_len", P), ("host_topk_idx", P), ("host_mem_len", P),
+        ("host_mem_docs", P), ("copy_stream", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class DecodeArgs(ctypes.Structure):
     _fields_ = [
         ("dtype", I32), ("batch", I32), ("n_q_heads", I32), ("n_kv_heads", I32), ("head_dim", I32),
@@ -78,7 +88,8 @@ class AttendArgs(ctypes.Structure):
     ]
 
 
-EXPORTS = ("msa_pool_encode", "msa_route", "msa_route_workspace_bytes", "msa_doc_map_bytes", "msa_doc_map",
+EXPORTS = ("msa_pool_encode", "msa_route", "msa_route_workspace_bytes", "msa_assemble", "msa_assemble_workspace_bytes",
+           "msa_doc_map_bytes", "msa_doc_map",
            "msa_sparse_decode", "msa_sparse_decode_noalloc",
            "msa_decode_workspace_bytes", "msa_sparse_attend", "msa_attend_workspace_bytes", "msa_last_error",
            "msa_version")
@@ -104,6 +115,10 @@ def load(path=None):
     lib.msa_sparse_decode.restype = ctypes.c_int
     lib.msa_sparse_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), P]
     lib.msa_sparse_decode_noalloc.restype = ctypes.c_int
+    lib.msa_assemble.argtypes = [ctypes.POINTER(AssembleArgs), P]
+    lib.msa_assemble.restype = ctypes.c_int
+    lib.msa_assemble_workspace_bytes.argtypes = [I32, I32]
+    lib.msa_assemble_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_route_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I64, I32]
     lib.msa_route_workspace_bytes.restype = ctypes.c_size_t
     lib.msa_doc_map_bytes.argtypes = [I64]
@@ -262,6 +277,49 @@ class Assembly:
                    torch.zeros(batch, dtype=torch.int32, pin_memory=True), copy_stream=copy_stream, mode=mode)
 
 
+def _fill_assembly(a, asm, stream):
+    """The assembly fields of RouteArgs / AssembleArgs from an Assembly."""
+    a.host_kv = _hptr(asm.host_kv, "host_kv", pinned=asm.mode == "kernel")
+    a.host_doc_pool_off = _hptr(asm.host_doc_pool_off, "host_doc_pool_off")
+    a.kv_dtype = dtype_code(asm.host_kv.dtype)
+    a.n_kv_heads = asm.host_kv.shape[2]
+    a.head_dim = asm.host_kv.shape[3]
+    a.mem_cap = asm.mem_kv.shape[1]
+    a.append = 1 if asm.append else 0
+    a.gather_mode = MSA_GATHER_KERNEL if asm.mode == "kernel" else MSA_GATHER_COPIES
+    a.mem_kv = _dptr(asm.mem_kv, "mem_kv")
+    a.mem_len = _dptr(asm.mem_len, "mem_len")
+    a.host_topk_idx = _hptr(asm.host_topk_idx, "host_topk_idx")
+    a.host_mem_len = _hptr(asm.host_mem_len, "host_mem_len")
+    a.host_mem_docs = _hptr(asm.host_mem_docs, "host_mem_docs")
+    cs = asm.copy_stream if asm.copy_stream is not None else stream
+    a.copy_stream = _stream(cs)
+
+
+def assemble_workspace_bytes(batch, top_k):
+    return int(load().msa_assemble_workspace_bytes(batch, top_k))
+
+
+def assemble(topk_idx, doc_pool_off, assembly, workspace=None, stream=None):
+    """msa_assemble: copy the documents topk_idx [B, k] (int32 device, rank
+    order) name into assembly.mem_kv, as msa_route's assembly does.
+    doc_pool_off: int64 device [n_docs+1] (the kernel mode reads it there).
+    Returns assembly.mem_len."""
+    b, k = topk_idx.shape
+    n_docs = doc_pool_off.numel() - 1
+    a = AssembleArgs(batch=b, top_k=k, n_docs=n_docs, n_pool=assembly.host_kv.shape[0],
+                     topk_idx=_dptr(topk_idx, "topk_idx"), doc_pool_off=_dptr(doc_pool_off, "doc_pool_off"))
+    _fill_assembly(a, assembly, stream)
+    if assembly.mode == "kernel":
+        if workspace is None:
+            workspace = torch.empty(max(assemble_workspace_bytes(b, k), 16), dtype=torch.uint8,
+                                    device=topk_idx.device)
+        a.workspace = _dptr(workspace, "workspace")
+        a.workspace_bytes = workspace.numel()
+    _check(load().msa_assemble(ctypes.byref(a), _stream(stream)))
+    return assembly.mem_len
+
+
 def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, topk_score=None,
           workspace=None, assembly=None, stream=None, prof_events=None, kr_layout="rows", n_pool=None,
           doc_map=None):
@@ -296,22 +354,7 @@ def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, to
                   topk_idx=_dptr(topk_idx, "topk_idx"), topk_score=_dptr(topk_score, "topk_score"),
                   workspace=_dptr(workspace, "workspace"), workspace_bytes=workspace.numel(), kr_layout=lay)
     if assembly is not None:
-        asm = assembly
-        a.host_kv = _hptr(asm.host_kv, "host_kv", pinned=asm.mode == "kernel")
-        a.host_doc_pool_off = _hptr(asm.host_doc_pool_off, "host_doc_pool_off")
-        a.kv_dtype = dtype_code(asm.host_kv.dtype)
-        a.n_kv_heads = asm.host_kv.shape[2]
-        a.head_dim = asm.host_kv.shape[3]
-        a.mem_cap = asm.mem_kv.shape[1]
-        a.append = 1 if asm.append else 0
-        a.gather_mode = MSA_GATHER_KERNEL if asm.mode == "kernel" else MSA_GATHER_COPIES
-        a.mem_kv = _dptr(asm.mem_kv, "mem_kv")
-        a.mem_len = _dptr(asm.mem_len, "mem_len")
-        a.host_topk_idx = _hptr(asm.host_topk_idx, "host_topk_idx")
-        a.host_mem_len = _hptr(asm.host_mem_len, "host_mem_len")
-        a.host_mem_docs = _hptr(asm.host_mem_docs, "host_mem_docs")
-        cs = asm.copy_stream if asm.copy_stream is not None else stream
-        a.copy_stream = _stream(cs)
+        _fill_assembly(a, assembly, stream)
     if prof_events is not None:
         a.prof_event_begin, a.prof_event_end = prof_events
     if doc_map is not None:

@@ -62,6 +62,114 @@ hipError_t thread_events(ThreadEvents **out) {
   return hipSuccess;
 }
 
+// The assembly half of msa_route's arguments, as msa_assemble takes them.
+msa_assemble_args assembly_of(const msa_route_args &a) {
+  msa_assemble_args x = {};
+  x.batch = a.batch;
+  x.top_k = a.top_k;
+  x.n_docs = a.n_docs;
+  x.kv_dtype = a.kv_dtype;
+  x.n_pool = a.n_pool;
+  x.topk_idx = a.topk_idx;
+  x.doc_pool_off = a.doc_pool_off;
+  x.host_kv = a.host_kv;
+  x.host_doc_pool_off = a.host_doc_pool_off;
+  x.n_kv_heads = a.n_kv_heads;
+  x.head_dim = a.head_dim;
+  x.mem_cap = a.mem_cap;
+  x.append = a.append;
+  x.gather_mode = a.gather_mode;
+  x.mem_kv = a.mem_kv;
+  x.mem_len = a.mem_len;
+  x.host_topk_idx = a.host_topk_idx;
+  x.host_mem_len = a.host_mem_len;
+  x.host_mem_docs = a.host_mem_docs;
+  x.copy_stream = a.copy_stream;
+  return x;
+}
+
+// Checks of the assembly arguments (msa_route with assembly, msa_assemble);
+// the kernel mode also needs host_kv's device mapping, returned in *host_kv_dev.
+int check_assembly(const char *who, const msa_assemble_args &x, void **host_kv_dev) {
+  const bool kernel_gather = x.gather_mode == MSA_GATHER_KERNEL;
+  if (x.gather_mode != MSA_GATHER_COPIES && !kernel_gather)
+    return fail(MSA_ERR_INVALID_ARG, "%s: bad gather_mode %d", who, x.gather_mode);
+  if (!x.host_doc_pool_off || !x.mem_kv || !x.mem_len)
+    return fail(MSA_ERR_INVALID_ARG, "%s: assembly needs host_doc_pool_off, mem_kv and mem_len", who);
+  if (!kernel_gather && (!x.host_topk_idx || !x.host_mem_len))
+    return fail(MSA_ERR_INVALID_ARG, "%s: copy assembly needs host_topk_idx and host_mem_len", who);
+  if (!dtype_ok(x.kv_dtype)) return fail(MSA_ERR_INVALID_ARG, "%s: bad kv_dtype %d", who, x.kv_dtype);
+  if (x.n_kv_heads < 1 || x.head_dim < 1 || x.mem_cap < 0)
+    return fail(MSA_ERR_INVALID_ARG, "%s: assembly needs n_kv_heads, head_dim >= 1, mem_cap >= 0", who);
+  if (x.append && !kernel_gather) {
+    for (int b = 0; b < x.batch; ++b)
+      if (x.host_mem_len[b] < 0 || x.host_mem_len[b] > x.mem_cap)
+        return fail(MSA_ERR_INVALID_ARG, "%s: host_mem_len[%d] = %d outside [0, mem_cap]", who, b, x.host_mem_len[b]);
+  }
+  *host_kv_dev = nullptr;
+  if (kernel_gather) {
+    const size_t row_bytes = 2 * (size_t)x.n_kv_heads * x.head_dim * elt_size(x.kv_dtype);
+    if (!aligned16(x.host_kv) || !aligned16(x.mem_kv) || row_bytes % 16 != 0)
+      return fail(MSA_ERR_INVALID_ARG, "%s: kernel assembly needs 16-byte aligned host_kv, mem_kv and rows", who);
+    if (hipHostGetDevicePointer(host_kv_dev, const_cast<void *>(x.host_kv), 0) != hipSuccess || !*host_kv_dev) {
+      (void)hipGetLastError();
+      return fail(MSA_ERR_INVALID_ARG, "%s: host_kv is not device-mapped pinned memory", who);
+    }
+  }
+  return MSA_OK;
+}
+
+// Host-driven assembly: the top-k ids to the host (after the work queued on
+// s), then one hipMemcpyAsync per document on the copy stream, and s waits
+// for the copies.  Blocks the calling thread until the ids have landed.
+int copy_assembly(const char *who, const msa_assemble_args &x, hipStream_t s) {
+  ThreadEvents *ev = nullptr;
+  hipError_t e;
+  if ((e = thread_events(&ev)) != hipSuccess) return fail(MSA_ERR_HIP, "%s events: %s", who, hipGetErrorString(e));
+  const size_t idx_bytes = sizeof(int32_t) * (size_t)x.batch * x.top_k;
+  if ((e = hipMemcpyAsync(x.host_topk_idx, x.topk_idx, idx_bytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return fail(MSA_ERR_HIP, "%s top-k to host: %s", who, hipGetErrorString(e));
+  if ((e = hipEventRecord(ev->topk, s)) != hipSuccess)
+    return fail(MSA_ERR_HIP, "%s event record: %s", who, hipGetErrorString(e));
+  if ((e = hipEventSynchronize(ev->topk)) != hipSuccess)
+    return fail(MSA_ERR_HIP, "%s wait for top-k: %s", who, hipGetErrorString(e));
+
+  hipStream_t cs = reinterpret_cast<hipStream_t>(x.copy_stream);
+  const size_t row_bytes = 2 * (size_t)x.n_kv_heads * x.head_dim * elt_size(x.kv_dtype);
+  const char *src = reinterpret_cast<const char *>(x.host_kv);
+  char *dst = reinterpret_cast<char *>(x.mem_kv);
+  const int64_t *off = x.host_doc_pool_off;
+  for (int b = 0; b < x.batch; ++b) {
+    int64_t len = x.append ? x.host_mem_len[b] : 0;
+    int taken = 0;
+    for (int r = 0; r < x.top_k; ++r) {
+      const int32_t d = x.host_topk_idx[(size_t)b * x.top_k + r];
+      if (d < 0 || d >= x.n_docs) break;
+      const int64_t r0 = off[d], r1 = off[d + 1];
+      if (r0 < 0 || r1 < r0 || r1 > x.n_pool) break;
+      const int64_t rows = r1 - r0;
+      if (len + rows > x.mem_cap) break;
+      if (rows > 0) {
+        e = hipMemcpyAsync(dst + ((size_t)b * x.mem_cap + len) * row_bytes, src + (size_t)r0 * row_bytes,
+                           (size_t)rows * row_bytes, hipMemcpyHostToDevice, cs);
+        if (e != hipSuccess) return fail(MSA_ERR_HIP, "%s gather copy: %s", who, hipGetErrorString(e));
+      }
+      len += rows;
+      ++taken;
+    }
+    x.host_mem_len[b] = (int32_t)len;
+    if (x.host_mem_docs) x.host_mem_docs[b] = taken;
+  }
+  if ((e = hipMemcpyAsync(x.mem_len, x.host_mem_len, sizeof(int32_t) * x.batch, hipMemcpyHostToDevice, cs)) !=
+      hipSuccess)
+    return fail(MSA_ERR_HIP, "%s mem_len copy: %s", who, hipGetErrorString(e));
+  if ((e = hipEventRecord(ev->copies, cs)) != hipSuccess)
+    return fail(MSA_ERR_HIP, "%s event record: %s", who, hipGetErrorString(e));
+  if ((e = hipStreamWaitEvent(s, ev->copies, 0)) != hipSuccess)
+    return fail(MSA_ERR_HIP, "%s stream wait: %s", who, hipGetErrorString(e));
+  return MSA_OK;
+}
+
 }  // namespace
 
 const DeviceInfo &device_info() {
@@ -211,33 +319,10 @@ int msa_route(const msa_route_args *a, void *stream) {
   const bool assemble = a->host_kv != nullptr;
   const bool kernel_gather = assemble && a->gather_mode == MSA_GATHER_KERNEL;
   void *host_kv_dev = nullptr;
+  const msa_assemble_args x = assembly_of(*a);
   if (assemble) {
-    if (a->gather_mode != MSA_GATHER_COPIES && a->gather_mode != MSA_GATHER_KERNEL)
-      return fail(MSA_ERR_INVALID_ARG, "msa_route: bad gather_mode %d", a->gather_mode);
-    if (!a->host_doc_pool_off || !a->mem_kv || !a->mem_len)
-      return fail(MSA_ERR_INVALID_ARG, "msa_route: assembly needs host_doc_pool_off, mem_kv and mem_len");
-    if (!kernel_gather && (!a->host_topk_idx || !a->host_mem_len))
-      return fail(MSA_ERR_INVALID_ARG, "msa_route: copy assembly needs host_topk_idx and host_mem_len");
-    if (!dtype_ok(a->kv_dtype)) return fail(MSA_ERR_INVALID_ARG, "msa_route: bad kv_dtype %d", a->kv_dtype);
-    if (a->n_kv_heads < 1 || a->head_dim < 1 || a->mem_cap < 0)
-      return fail(MSA_ERR_INVALID_ARG, "msa_route: assembly needs n_kv_heads, head_dim >= 1, mem_cap >= 0");
-    if (a->append && !kernel_gather) {
-      for (int b = 0; b < a->batch; ++b)
-        if (a->host_mem_len[b] < 0 || a->host_mem_len[b] > a->mem_cap)
-          return fail(MSA_ERR_INVALID_ARG, "msa_route: host_mem_len[%d] = %d outside [0, mem_cap]", b,
-                      a->host_mem_len[b]);
-    }
-    if (kernel_gather) {
-      const size_t row_bytes = 2 * (size_t)a->n_kv_heads * a->head_dim * elt_size(a->kv_dtype);
-      if (!aligned16(a->host_kv) || !aligned16(a->mem_kv) || row_bytes % 16 != 0)
-        return fail(MSA_ERR_INVALID_ARG, "msa_route: kernel assembly needs 16-byte aligned host_kv, mem_kv "
-                                         "and rows");
-      if (hipHostGetDevicePointer(&host_kv_dev, const_cast<void *>(a->host_kv), 0) != hipSuccess ||
-          !host_kv_dev) {
-        (void)hipGetLastError();
-        return fail(MSA_ERR_INVALID_ARG, "msa_route: host_kv is not device-mapped pinned memory");
-      }
-    }
+    const int st = check_assembly("msa_route", x, &host_kv_dev);
+    if (st != MSA_OK) return st;
   }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -253,48 +338,34 @@ int msa_route(const msa_route_args *a, void *stream) {
   hipError_t e = launch_route(*a, ws, host_kv_dev, s);
   if (e != hipSuccess) return hip_fail(e, "msa_route launch");
   if (!assemble || kernel_gather) return MSA_OK;
+  return copy_assembly("msa_route", x, s);
+}
 
-  // ---- host-driven assembly: indices to the host, then one copy per document ----
-  ThreadEvents *ev = nullptr;
-  if ((e = thread_events(&ev)) != hipSuccess) return hip_fail(e, "msa_route events");
-  const size_t idx_bytes = sizeof(int32_t) * (size_t)a->batch * a->top_k;
-  if ((e = hipMemcpyAsync(a->host_topk_idx, a->topk_idx, idx_bytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
-    return hip_fail(e, "msa_route top-k to host");
-  if ((e = hipEventRecord(ev->topk, s)) != hipSuccess) return hip_fail(e, "msa_route event record");
-  if ((e = hipEventSynchronize(ev->topk)) != hipSuccess) return hip_fail(e, "msa_route wait for top-k");
+size_t msa_assemble_workspace_bytes(int32_t batch, int32_t top_k) {
+  if (batch < 1 || top_k < 1) return 0;
+  return ((size_t)batch * top_k * sizeof(GatherPlan) + 255) & ~(size_t)255;
+}
 
-  hipStream_t cs = reinterpret_cast<hipStream_t>(a->copy_stream);
-  const size_t row_bytes = 2 * (size_t)a->n_kv_heads * a->head_dim * elt_size(a->kv_dtype);
-  const char *src = reinterpret_cast<const char *>(a->host_kv);
-  char *dst = reinterpret_cast<char *>(a->mem_kv);
-  const int64_t *off = a->host_doc_pool_off;
-  for (int b = 0; b < a->batch; ++b) {
-    int64_t len = a->append ? a->host_mem_len[b] : 0;
-    int taken = 0;
-    for (int r = 0; r < a->top_k; ++r) {
-      const int32_t d = a->host_topk_idx[(size_t)b * a->top_k + r];
-      if (d < 0 || d >= a->n_docs) break;
-      const int64_t r0 = off[d], r1 = off[d + 1];
-      if (r0 < 0 || r1 < r0 || r1 > a->n_pool) break;
-      const int64_t rows = r1 - r0;
-      if (len + rows > a->mem_cap) break;
-      if (rows > 0) {
-        e = hipMemcpyAsync(dst + ((size_t)b * a->mem_cap + len) * row_bytes, src + (size_t)r0 * row_bytes,
-                           (size_t)rows * row_bytes, hipMemcpyHostToDevice, cs);
-        if (e != hipSuccess) return hip_fail(e, "msa_route gather copy");
-      }
-      len += rows;
-      ++taken;
-    }
-    a->host_mem_len[b] = (int32_t)len;
-    if (a->host_mem_docs) a->host_mem_docs[b] = taken;
-  }
-  if ((e = hipMemcpyAsync(a->mem_len, a->host_mem_len, sizeof(int32_t) * a->batch, hipMemcpyHostToDevice, cs)) !=
-      hipSuccess)
-    return hip_fail(e, "msa_route mem_len copy");
-  if ((e = hipEventRecord(ev->copies, cs)) != hipSuccess) return hip_fail(e, "msa_route event record");
-  if ((e = hipStreamWaitEvent(s, ev->copies, 0)) != hipSuccess) return hip_fail(e, "msa_route stream wait");
-  return MSA_OK;
+int msa_assemble(const msa_assemble_args *a, void *stream) {
+  if (!a) return fail(MSA_ERR_INVALID_ARG, "msa_assemble: args is NULL");
+  if (a->batch < 1 || a->n_docs < 1 || a->n_pool < a->n_docs || !a->topk_idx || !a->host_kv)
+    return fail(MSA_ERR_INVALID_ARG, "msa_assemble: need batch, n_docs >= 1, n_pool >= n_docs, topk_idx, host_kv");
+  if (a->n_docs > 0x7ffffffe) return fail(MSA_ERR_UNSUPPORTED, "msa_assemble: too many documents");
+  if (a->top_k < 1 || a->top_k > a->n_docs)
+    return fail(MSA_ERR_INVALID_ARG, "msa_assemble: need 1 <= top_k (%d) <= n_docs (%d)", a->top_k, a->n_docs);
+  if (a->top_k > kMaxTopK) return fail(MSA_ERR_UNSUPPORTED, "msa_assemble: top_k > %d", kMaxTopK);
+  void *host_kv_dev = nullptr;
+  const int st = check_assembly("msa_assemble", *a, &host_kv_dev);
+  if (st != MSA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (a->gather_mode == MSA_GATHER_COPIES) return copy_assembly("msa_assemble", *a, s);
+  const size_t need = msa_assemble_workspace_bytes(a->batch, a->top_k);
+  if (!a->doc_pool_off) return fail(MSA_ERR_INVALID_ARG, "msa_assemble: kernel assembly needs doc_pool_off");
+  if (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace))
+    return fail(MSA_ERR_WORKSPACE, "msa_assemble: workspace needs %zu bytes (16-byte aligned), got %zu", need,
+                a->workspace ? a->workspace_bytes : (size_t)0);
+  const hipError_t e = launch_assemble(*a, reinterpret_cast<GatherPlan *>(a->workspace), host_kv_dev, s);
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "msa_assemble launch");
 }
 
 // bf16 decode runs the block-attention kernel with one query token (fp32

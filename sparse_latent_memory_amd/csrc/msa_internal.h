@@ -138,6 +138,9 @@ inline size_t doc_map_bits_offset(int64_t n_pool) {
   return ((size_t)4 * (size_t)((n_pool + 15) / 16) + 255) & ~(size_t)255;
 }
 hipError_t launch_select(const msa_route_args &a, const RouteWs &ws, const void *host_kv_dev, hipStream_t s);
+// msa_assemble in the device-side mode: the copy plan from given top-k ids,
+// then the gather (plan: [B, k] in the caller's workspace)
+hipError_t launch_assemble(const msa_assemble_args &a, GatherPlan *plan, const void *host_kv_dev, hipStream_t s);
 
 size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t hr, int32_t dr,
                        int32_t n_docs, int64_t n_pool, int32_t top_k, void *base, RouteWs *ws);

@@ -270,6 +270,82 @@ __global__ __launch_bounds__(kDocsPerBlock) void doc_parts_kernel(
 }
 
 // --------------------------------------------------------------------------
+// Context assembly plan of one query: its documents in rank order while they
+// fit in the memory after len0 rows; the first one that does not fit closes
+// the plan for every later rank.  doc(r) is rank r's document, or a negative
+// value, which ends the list.  Writes plan_b[r] for every rank (rows 0 when
+// not copied) and the new length.  Every thread of the block calls it; k <= 64
+// runs in wave 0 alone (a prefix over lanes), larger k serially over LDS
+// (r0s, prow, pdst: k entries each).
+// --------------------------------------------------------------------------
+template <typename DocOf>
+__device__ __forceinline__ void assembly_plan(DocOf doc, int k, const int64_t *__restrict__ pool_off, int n_docs,
+                                              int64_t n_pool, int mem_cap, int64_t len0, GatherPlan *plan_b,
+                                              int32_t *mem_len_b, uint64_t *r0s, int32_t *prow, int32_t *pdst) {
+  const int tid = threadIdx.x;
+  // rank r's first row and row count; a missing document counts as too large
+  auto rows_of = [&](int r, int64_t *r0) -> int64_t {
+    const int d = doc(r);
+    if (d < 0) { *r0 = 0; return (int64_t)mem_cap + 1; }
+    const int dd = min(d, n_docs - 1);
+    *r0 = clamp_row(pool_off[dd], n_pool);
+    const int64_t r1 = max(*r0, clamp_row(pool_off[dd + 1], n_pool));
+    return min(r1 - *r0, (int64_t)mem_cap + 1);
+  };
+  if (k <= 64) {
+    if ((tid >> 6) != 0) return;
+    const int r = tid;
+    int64_t r0 = 0, pr = 0;
+    if (r < k) pr = rows_of(r, &r0);
+    int64_t inc = pr;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up((long)inc, o, 64);
+      if (r >= o) inc += y;
+    }
+    const bool open = r < k && len0 + inc <= mem_cap;
+    GatherPlan p = {0, 0, 0};
+    if (open) {
+      p.src_row = r0;
+      p.rows = (int32_t)pr;
+      p.dst_row = (int32_t)(len0 + inc - pr);
+    }
+    if (r < k) plan_b[r] = p;
+    const uint64_t end = __ballot(open);                   // open ranks are a prefix
+    const int n_open = __popcll(end);
+    const int64_t len = n_open ? len0 + __shfl(inc, n_open - 1, 64) : len0;
+    if (r == 0) *mem_len_b = (int32_t)len;
+    return;
+  }
+  for (int r = tid; r < k; r += blockDim.x) {              // every rank's offsets loaded in parallel
+    int64_t r0 = 0;
+    prow[r] = (int32_t)rows_of(r, &r0);
+    r0s[r] = (uint64_t)r0;
+  }
+  __syncthreads();
+  if (tid == 0) {                                          // prefix over LDS only
+    int64_t len = len0;
+    bool open = true;
+    for (int r = 0; r < k; ++r) {
+      open = open && len + prow[r] <= mem_cap;
+      pdst[r] = open ? (int32_t)len : -1;
+      if (open) len += prow[r];
+    }
+    *mem_len_b = (int32_t)len;
+  }
+  __syncthreads();
+  for (int r = tid; r < k; r += blockDim.x) {
+    GatherPlan p = {0, 0, 0};
+    if (pdst[r] >= 0) {
+      p.src_row = (int64_t)r0s[r];
+      p.rows = prow[r];
+      p.dst_row = pdst[r];
+    }
+    plan_b[r] = p;
+  }
+}
+
+// --------------------------------------------------------------------------
 // 2. exact top-k per query
 // --------------------------------------------------------------------------
 // A separate launch rather than a last-block-done tail on the kernel above:
@@ -569,72 +645,24 @@ __global__ __launch_bounds__(kDocsPerBlock) void topk_final_kernel(
     topk_score[(int64_t)b * k + i] = key_score((uint32_t)(x >> 32));
   }
   if (!plan) return;
-  // ---- context assembly plan: documents in rank order while they fit ----
-  if (k <= 64) {
-    // one wave: rank r = lane; a document is placed iff the inclusive
-    // prefix of the row counts still fits (the counts are non-negative, so
-    // the first one that does not fit closes the plan for every later rank)
-    if (wave == 0) {
-      const int r = tid;
-      int64_t r0 = 0, pr = 0;
-      if (r < k) {
-        const int dd = min(max((int)(0xffffffffu - (uint32_t)(top[r] & 0xffffffffu)), 0), n_docs - 1);
-        r0 = clamp_row(pool_off[dd], n_pool);
-        const int64_t r1 = max(r0, clamp_row(pool_off[dd + 1], n_pool));
-        pr = min(r1 - r0, (int64_t)mem_cap + 1);
-      }
-      int64_t inc = pr;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int64_t y = __shfl_up((long)inc, o, 64);
-        if (r >= o) inc += y;
-      }
-      const int64_t len0 = append ? max(0, min(len_in, mem_cap)) : 0;
-      const bool open = r < k && len0 + inc <= mem_cap;
-      GatherPlan p = {0, 0, 0};
-      if (open) {
-        p.src_row = r0;
-        p.rows = (int32_t)pr;
-        p.dst_row = (int32_t)(len0 + inc - pr);
-      }
-      if (r < k) plan[(int64_t)b * k + r] = p;
-      const uint64_t end = __ballot(open);                 // open ranks are a prefix
-      const int n_open = __popcll(end);
-      const int64_t len = n_open ? len0 + __shfl(inc, n_open - 1, 64) : len0;
-      if (r == 0) mem_len[b] = (int32_t)len;
-    }
-    return;
-  }
   __shared__ int32_t prow[kMaxTopK], pdst[kMaxTopK];
-  __syncthreads();                       // top[] is reused below
-  for (int r = tid; r < k; r += blockDim.x) {   // every rank's offsets loaded in parallel
-    const int dd = min(max((int)(0xffffffffu - (uint32_t)(top[r] & 0xffffffffu)), 0), n_docs - 1);
-    const int64_t r0 = clamp_row(pool_off[dd], n_pool);
-    const int64_t r1 = max(r0, clamp_row(pool_off[dd + 1], n_pool));
-    top[r] = (uint64_t)r0;
-    prow[r] = (int32_t)min(r1 - r0, (int64_t)mem_cap + 1);
-  }
-  __syncthreads();
-  if (tid == 0) {                        // prefix over LDS only
-    int64_t len = append ? max(0, min(len_in, mem_cap)) : 0;
-    bool open = true;
-    for (int r = 0; r < k; ++r) {
-      open = open && len + prow[r] <= mem_cap;
-      pdst[r] = open ? (int32_t)len : -1;
-      if (open) len += prow[r];
-    }
-    mem_len[b] = (int32_t)len;
-  }
-  __syncthreads();
-  for (int r = tid; r < k; r += blockDim.x) {
-    GatherPlan p = {0, 0, 0};
-    if (pdst[r] >= 0) {
-      p.src_row = (int64_t)top[r];
-      p.rows = prow[r];
-      p.dst_row = pdst[r];
-    }
-    plan[(int64_t)b * k + r] = p;
-  }
+  __syncthreads();                       // top[] is reused by the plan
+  const int64_t len0 = append ? max(0, min(len_in, mem_cap)) : 0;
+  assembly_plan([&](int r) { return (int)(0xffffffffu - (uint32_t)(top[r] & 0xffffffffu)); }, k, pool_off, n_docs,
+                n_pool, mem_cap, len0, plan + (int64_t)b * k, mem_len + b, top, prow, pdst);
+}
+
+// Context assembly from given top-k ids (msa_assemble): the plan alone.
+__global__ __launch_bounds__(kDocsPerBlock) void assemble_plan_kernel(
+    const int32_t *__restrict__ topk_idx, const int64_t *__restrict__ pool_off, GatherPlan *__restrict__ plan,
+    int32_t *__restrict__ mem_len, int mem_cap, int append, int n_docs, int64_t n_pool, int k) {
+  __shared__ uint64_t r0s[kMaxTopK];
+  __shared__ int32_t prow[kMaxTopK], pdst[kMaxTopK];
+  const int b = blockIdx.x;
+  const int64_t len0 = append ? max(0, min(mem_len[b], mem_cap)) : 0;
+  const int32_t *ids = topk_idx + (int64_t)b * k;
+  assembly_plan([&](int r) { const int d = ids[r]; return d >= 0 && d < n_docs ? d : -1; }, k, pool_off, n_docs,
+                n_pool, mem_cap, len0, plan + (int64_t)b * k, mem_len + b, r0s, prow, pdst);
 }
 
 // --------------------------------------------------------------------------
@@ -665,6 +693,19 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4 *__restrict__ h
 }
 
 }  // namespace
+
+hipError_t launch_assemble(const msa_assemble_args &a, GatherPlan *plan, const void *host_kv_dev, hipStream_t s) {
+  hipLaunchKernelGGL(assemble_plan_kernel, dim3(a.batch), dim3(kDocsPerBlock), 0, s, a.topk_idx, a.doc_pool_off, plan,
+                     a.mem_len, a.mem_cap, a.append, a.n_docs, a.n_pool, a.top_k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t elt = a.kv_dtype == MSA_BF16 ? 2 : 4;
+  const int64_t row_vecs = (int64_t)(2 * (size_t)a.n_kv_heads * a.head_dim * elt / 16);
+  hipLaunchKernelGGL(gather_kernel, dim3(a.top_k, a.batch), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4 *>(host_kv_dev), reinterpret_cast<u32x4 *>(a.mem_kv), plan,
+                     a.top_k, a.mem_cap, row_vecs);
+  return hipGetLastError();
+}
 
 hipError_t launch_doc_map(const int64_t *pool_off, int32_t n_docs, int64_t n_pool, int32_t *tile_doc,
                           uint32_t *tile_bits, hipStream_t s) {

@@ -8,7 +8,8 @@ Tolerances (floating point; integer/byte work is compared exactly):
 * top-k: with tau = 2e-3 and the oracle's k-th score s_k, every document with
   oracle score > s_k + tau is selected and every selected document has
   oracle score >= s_k - tau; where the gap exceeds tau the sets agree.
-* decode: per (query, head) ||g - r|| <= 2e-2 ||r|| for bf16, 1e-4 for fp32.
+* decode: per (query, head) ||g - r|| <= 2e-2 ||r|| for bf16, 1e-4 for fp32;
+  the log-sum-exp within lse_bound (the rounding the arithmetic allows).
 """
 
 import numpy as np
@@ -116,3 +117,31 @@ def check_decode(got, ref, dtype, what=""):
     bad = err > lim
     assert not bad.any(), f"{what}: {bad.sum()} heads over bound; worst ratio {np.max(err / lim):.3g} " \
                           f"at {np.argwhere(bad)[:3].tolist()}"
+
+
+def lse_bound(q, mem_k, mem_len, local_k, local_len, dtype):
+    """Per (query, head): the largest log-sum-exp error the decode's
+    arithmetic allows.  bf16: each locally rotated key is rounded to bf16
+    once (|dk| <= 2^-9 |k|) and the rotated, scaled query is kept as two bf16
+    terms (|dq| <= 2^-16 |q|), so a logit moves by at most
+    scale |q| (2^-9 max|k_local| + 2^-16 max|k|), and the log-sum-exp by at
+    most the largest logit change; plus 1e-5 for fp32 sums.  fp32 inputs:
+    1e-4 (fp32 logits, exp2 and log2 of the vector units).
+    q [B, Hq, D]; mem_k [B, M_cap, Hkv, D] (or None); local_k [B, T_cap, Hkv, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    n_b, n_q, d = q.shape
+    if dtype != torch.bfloat16:
+        return np.full((n_b, n_q), 1e-4)
+    n_kv = np.asarray(local_k).shape[2]
+    grp = n_q // n_kv
+    out = np.empty((n_b, n_q))
+    for b in range(n_b):
+        kl = np.linalg.norm(np.asarray(local_k[b, :local_len[b]], dtype=np.float64), axis=-1)   # [T, Hkv]
+        km = (np.linalg.norm(np.asarray(mem_k[b, :mem_len[b]], dtype=np.float64), axis=-1)
+              if mem_k is not None and mem_len[b] > 0 else np.zeros((0, n_kv)))
+        for h in range(n_q):
+            g = h // grp
+            ml = kl[:, g].max() if kl.shape[0] else 0.0
+            ma = max(ml, km[:, g].max() if km.shape[0] else 0.0)
+            out[b, h] = np.linalg.norm(q[b, h]) / np.sqrt(d) * (2.0 ** -9 * ml + 2.0 ** -16 * ma) + 1e-5
+    return out

@@ -254,6 +254,48 @@ def test_route_assembly_arguments_checked_before_launch():
     assert b"kv_dtype" in lib.msa_last_error()
 
 
+def _assemble_args(**kw):
+    a = _lib.AssembleArgs(batch=1, top_k=4, n_docs=10, kv_dtype=1, n_pool=20, topk_idx=_p(), doc_pool_off=_p(),
+                          host_kv=_p(), host_doc_pool_off=_p(), n_kv_heads=8, head_dim=128, mem_cap=10, append=0,
+                          gather_mode=_lib.MSA_GATHER_COPIES, mem_kv=_p(), mem_len=_p(), host_topk_idx=_p(),
+                          host_mem_len=_p(), workspace=_p(), workspace_bytes=16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,code,msg", [
+    ({"batch": 0}, _lib.MSA_ERR_INVALID_ARG, b"batch"),
+    ({"topk_idx": None}, _lib.MSA_ERR_INVALID_ARG, b"topk_idx"),
+    ({"top_k": 11}, _lib.MSA_ERR_INVALID_ARG, b"top_k"),           # more than n_docs
+    ({"n_pool": 9}, _lib.MSA_ERR_INVALID_ARG, b"n_pool"),
+    ({"gather_mode": 7}, _lib.MSA_ERR_INVALID_ARG, b"gather_mode"),
+    ({"mem_kv": None}, _lib.MSA_ERR_INVALID_ARG, b"assembly needs"),
+    ({"host_topk_idx": None}, _lib.MSA_ERR_INVALID_ARG, b"copy assembly"),
+    ({"kv_dtype": 3}, _lib.MSA_ERR_INVALID_ARG, b"kv_dtype"),
+    ({"mem_cap": -1}, _lib.MSA_ERR_INVALID_ARG, b"mem_cap"),
+    ({"gather_mode": _lib.MSA_GATHER_KERNEL}, _lib.MSA_ERR_INVALID_ARG, b"device-mapped"),   # plain host address
+])
+def test_assemble_rejects_bad_arguments(kw, code, msg):
+    lib = _lib.load()
+    a = _assemble_args(**kw)
+    assert lib.msa_assemble(ctypes.byref(a), None) == code, lib.msa_last_error()
+    assert msg in lib.msa_last_error()
+    assert lib.msa_assemble(None, None) == _lib.MSA_ERR_INVALID_ARG
+
+
+@no_gpu
+def test_assemble_checks_appended_lengths_and_sizes_its_workspace():
+    lib = _lib.load()
+    lens = (ctypes.c_int32 * 1)(11)
+    a = _assemble_args(append=1, host_mem_len=ctypes.cast(lens, ctypes.c_void_p))
+    assert lib.msa_assemble(ctypes.byref(a), None) == _lib.MSA_ERR_INVALID_ARG     # 11 > mem_cap
+    assert b"host_mem_len" in lib.msa_last_error()
+    assert lib.msa_assemble_workspace_bytes(64, 8) >= 64 * 8 * 16               # one 16-byte plan entry per rank
+    assert lib.msa_assemble_workspace_bytes(0, 8) == 0
+
+
 def _decode_args(**kw):
     a = _lib.DecodeArgs(dtype=1, batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, mem_cap=128, local_cap=64,
                         q=_p(), mem_kv=_p(), mem_len=_p(), local_k=_p(), local_v=_p(), local_len=_p(),
