@@ -73,7 +73,17 @@ constexpr int kAMaxSplit = 4096;
 #ifndef MSA_ATT_ROTATE      // 1: rotate each query's split order by its index
 #define MSA_ATT_ROTATE 1
 #endif
+#ifndef MSA_ATT_BLOCK_QLO   // 1: the block kernel keeps the query's bf16 remainder term (two MFMAs per k-block)
+#define MSA_ATT_BLOCK_QLO 1
+#endif
+#ifndef MSA_ATT_BLOCK_NWMAX // largest number of query tiles (waves) per block-kernel workgroup: 4, 8 or 16
+#define MSA_ATT_BLOCK_NWMAX 16
+#endif
+#ifndef MSA_ATT_BLOCK_WAVES // waves per CU the block kernel's register budget aims for (one workgroup at least)
+#define MSA_ATT_BLOCK_WAVES 8
+#endif
 constexpr float kALog2e = 1.4426950408889634f;
+constexpr float kALazy = 8.f;   // block kernel: raise the running max only past this margin (log2 units)
 
 template <int D>
 struct AttnCfg {
@@ -92,6 +102,25 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ float amax4(const f32x4 &v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
 
+// x combined over the lanes l, l ^ 16, l ^ 32 and l ^ 48 - the four lanes
+// that hold one column of a 16x16 matrix-core result - with gfx950's lane
+// swaps (v_permlane32_swap exchanges the upper half of one operand with the
+// lower half of the other, v_permlane16_swap odd 16-lane rows with even
+// ones; given the same value twice, the two results hold x of lane l and of
+// lane l ^ 32, resp. l ^ 16, in every lane): VALU only, no LDS round trip.
+__device__ __forceinline__ float col_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // bf16 number e (0..7) of a 16-byte vector
 __device__ __forceinline__ uint32_t bf16_at(const u32x4 &v, int e) {
   const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
@@ -102,15 +131,16 @@ __device__ __forceinline__ uint32_t bf16_at(const u32x2 &v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// PREROT: the local keys come already rotated to their positions (o + i),
-// from rope_local_kernel; the kernel then rotates nothing but the query.
+// PREROT: the local keys come already rotated to their positions (o + i)
+// and the query rotated and scaled (rot_q, fp32), from rope_prepass_kernel;
+// the kernel then rotates nothing.
 template <int D, bool PREROT>
 __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
     const uint16_t *__restrict__ local_k, const uint16_t *__restrict__ local_v,
     const int32_t *__restrict__ local_len, const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc,
     float *__restrict__ part_ml, int B, int Tq, int Hq, int Hkv, int mem_cap, int local_cap, int n_mt, int n_split,
-    int split_len, int rps, float scale_log2, double log2_theta) {
+    int split_len, int rps, float scale_log2, double log2_theta, const float *__restrict__ rot_q) {
   using C = AttnCfg<D>;
   constexpr int KS = C::KS, HS = C::HS, NT = C::NT, DB = C::DB, VTS = C::VTS, HALF = D / 2;
   using VVec = typename std::conditional<DB == 8, u32x4, u32x2>::type;
@@ -221,25 +251,37 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
     u32x4 qhi[KS], qlo[KS];
     {
       float x[KS][8];
-      const uint16_t *src = q + (((int64_t)b * Tq + t_row) * Hq + g * G + (row_ok ? R % G : 0)) * D + 8 * grp;
+      const int64_t qrow = ((int64_t)b * Tq + t_row) * Hq + g * G + (row_ok ? R % G : 0);
+      if (PREROT) {
+        const float4 *src = reinterpret_cast<const float4 *>(rot_q + qrow * D + 8 * grp);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 v = row_ok ? ld16(src + 32 * s) : u32x4{0u, 0u, 0u, 0u};
-        float f[8];
-        Elt<uint16_t>::unpack(v, f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[s][e] = f[e];
-      }
-#pragma unroll
-      for (int s = 0; s < HS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float c, sn;
-          rope_phasor((double)o + (double)i_row, omega[32 * s + 8 * grp + e], &c, &sn);
-          const float x1 = x[s][e], x2 = x[s + HS][e];
-          x[s][e] = (x1 * c - x2 * sn) * scale_log2;
-          x[s + HS][e] = (x2 * c + x1 * sn) * scale_log2;
+        for (int s = 0; s < KS; ++s) {
+          const float4 u = row_ok ? src[8 * s] : float4{0.f, 0.f, 0.f, 0.f};
+          const float4 w = row_ok ? src[8 * s + 1] : float4{0.f, 0.f, 0.f, 0.f};
+          x[s][0] = u.x; x[s][1] = u.y; x[s][2] = u.z; x[s][3] = u.w;
+          x[s][4] = w.x; x[s][5] = w.y; x[s][6] = w.z; x[s][7] = w.w;
         }
+      } else {
+        const uint16_t *src = q + qrow * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4 v = row_ok ? ld16(src + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+          float f[8];
+          Elt<uint16_t>::unpack(v, f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[s][e] = f[e];
+        }
+#pragma unroll
+        for (int s = 0; s < HS; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float c, sn;
+            rope_phasor((double)o + (double)i_row, omega[32 * s + 8 * grp + e], &c, &sn);
+            const float x1 = x[s][e], x2 = x[s + HS][e];
+            x[s][e] = (x1 * c - x2 * sn) * scale_log2;
+            x[s + HS][e] = (x2 * c + x1 * sn) * scale_log2;
+          }
+      }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         float hi[8], lo[8];
@@ -419,272 +461,364 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
 }
 
 // Block form for launches with at least four 16-row query tiles per KV head
-// (prefill): the NW waves of a workgroup (4, 8 or 16, as many as there are
-// tiles) take NW consecutive tiles of one (query, KV head, key split) and
-// share every 16-key group, which the workgroup stages once in LDS - K row-major in padded rows (a wave's
-// A-operand reads of 16 rows hit 64 distinct banks), V transposed - double
-// buffered, one barrier per group.  Each thread loads one 16-byte piece of K
-// and four 4-byte pieces of V per group, so a group costs a workgroup what it
-// cost each wave before, and V is transposed once instead of four times.
-// Local keys come rotated (rope_local_kernel); only the query is rotated
-// here.  Scores, masking, the online softmax and the partials are those of
-// attend_kernel, per wave, with the wave's own causal key range; a wave
+// (prefill): a workgroup of NW waves takes NW consecutive tiles of one
+// (query, KV head, key split), one tile per wave, and shares every 64-key
+// group, which the workgroup stages once in LDS - K row-major in padded rows
+// (a wave's A-operand reads of 16 rows hit 64 distinct banks), V transposed
+// per 32-key half with its keys in the order of the score layout, so that a
+// lane's V^T operand is one 16-byte read - double buffered, one barrier per
+// group.  A group is taken in two 32-key halves: S^T = K Q^T for two
+// quarters, the online softmax over the half's 8 scores per lane (column
+// maxima over four lanes by lane swaps) and O^T += V^T P^T on
+// v_mfma_f32_16x16x32_bf16 with the two quarters as one 32-key step: P^T is
+// the softmax's output as it stands, and O^T keeps each query in one lane
+// column, so the rescale needs no exchange.  The running max is raised only
+// when a half's max exceeds it by more than kALazy (log2 units): the weights
+// then stay below 2^kALazy, and the result is the same function of the
+// scores (the merge and the normaliser use the max that was kept).  Local
+// keys and the query come rotated (rope_prepass_kernel), so nothing is
+// rotated here.
+// Scores, masking and the partials are those of attend_kernel, with the
+// tile's own causal key range: quarters past it are skipped, and a wave
 // whose tile lies past the last one loads and synchronises but stores
 // nothing.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 8 / NW) void attend_block_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len,
-    const uint16_t *__restrict__ local_k, const uint16_t *__restrict__ local_v,
-    const int32_t *__restrict__ local_len, const int32_t *__restrict__ pos_offset, float *__restrict__ part_acc,
+__global__ __launch_bounds__(NW * 64, MSA_ATT_BLOCK_WAVES / NW > 0 ? MSA_ATT_BLOCK_WAVES / NW : 1) void attend_block_kernel(
+    const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len, const uint16_t *__restrict__ local_k,
+    const uint16_t *__restrict__ local_v, const int32_t *__restrict__ local_len, float *__restrict__ part_acc,
     float *__restrict__ part_ml, int B, int Tq, int Hq, int Hkv, int mem_cap, int local_cap, int n_mt, int n_split,
-    int split_len, int rps, float scale_log2, double log2_theta) {
+    int split_len, int rps, const float *__restrict__ rot_q) {
   using C = AttnCfg<D>;
-  constexpr int KS = C::KS, HS = C::HS, NT = C::NT, VTS = C::VTS, HALF = D / 2;
+  constexpr int KS = C::KS, NT = C::NT;
+  constexpr int KG = 64;                                   // keys per group: four 16-key quarters, two halves
   constexpr int KRS = D + 8;                               // K row stride in LDS (bf16)
-  constexpr int KT = 16 * (D / 8);                         // threads loading K (one 16-byte piece each)
-  constexpr int VT = 4 * (D / 2);                          // threads loading V (4 keys x 2 dims each)
+  constexpr int VRS = 32 + 8;                              // V^T row (one dim, a half's 32 keys + pad), bf16
   constexpr int NTH = NW * 64;
-  static_assert(NTH >= KT && NTH >= VT, "every piece of a key group needs a loading thread");
-  __shared__ __align__(16) uint16_t ks[2][16 * KRS];
-  __shared__ __align__(16) uint16_t vt[2][D * VTS];
-  __shared__ double omega[HALF];
+  constexpr int KPN = KG * (D / 8), VPN = (KG / 4) * (D / 2);   // 16-byte K pieces, (4 keys x 2 dims) V pieces
+  constexpr int KPT = (KPN + NTH - 1) / NTH, VPT = (VPN + NTH - 1) / NTH;   // per thread per group
+  static_assert(KPN % NTH == 0 || KPN < NTH, "K pieces: whole rounds, or one partial round");
+  static_assert(VPN % NTH == 0 || VPN < NTH, "V pieces: whole rounds, or one partial round");
+  __shared__ __align__(16) uint16_t ks[2][KG * KRS];
+  // per half: [dim][slot], key 32 h + 16 jj + 4 q + r of the group in slot
+  // 8 q + 4 jj + r - the k-slot that lane group q gives it in P^T
+  __shared__ __align__(16) uint16_t vt[2][2][D * VRS];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // work item of the workgroup: (query, NW-tile group, split) of KV head g
-  const int n_mt4 = (n_mt + NW - 1) / NW;
+  const int n_tg = (n_mt + NW - 1) / NW;
   const int g = (int)(blockIdx.x % Hkv);
   int64_t r = (int64_t)(blockIdx.x / Hkv);
-  if (r >= (int64_t)B * n_mt4 * n_split) return;          // the whole workgroup: no barrier is left waiting
+  if (r >= (int64_t)B * n_tg * n_split) return;           // the whole workgroup: no barrier is left waiting
   const int split_i = (int)(r % n_split);
   r /= n_split;
-  const int mt4 = (int)(r % n_mt4);
-  const int b = (int)(r / n_mt4);
+  const int tgi = (int)(r % n_tg);
+  const int b = (int)(r / n_tg);
 #if MSA_ATT_ROTATE
   const int split = (int)((split_i + 5LL * b) % n_split);
 #else
   const int split = split_i;
 #endif
-  const int mt = NW * mt4 + wave;
-  const bool tile_ok = mt < n_mt;
   const int G = Hq / Hkv;
   const int M = max(0, min(mem_len[b], mem_cap));
   const int T = max(0, min(local_len[b], local_cap));
-  const int o = pos_offset[b];
   const int n_rows = Tq * G;
   const int col = lane & 15, grp = lane >> 4;
-  const int R = mt * 16 + col;
-  const bool row_ok = tile_ok && R < n_rows;
-  const int t_row = row_ok ? R / G : 0;
-  const int i_row = T - Tq + t_row;
-  const int i_first = T - Tq + (mt * 16) / G;
   // keys a tile sees: the memory, then local tokens up to its last token
   auto key_end_of = [&](int tile) {
     const int t_last = min(Tq - 1, (tile * 16 + 15) / G);
     return M + max(0, min(T, T - Tq + t_last + 1));
   };
   const int k_begin = split * split_len;
-  const int k_end_g = min(key_end_of(min(NW * mt4 + NW - 1, n_mt - 1)), k_begin + split_len);   // the workgroup's
-  const int k_end = tile_ok ? min(key_end_of(mt), k_begin + split_len) : k_begin;        // this wave's
-  const int64_t slot = (((int64_t)b * Hkv + g) * n_mt + mt) * n_split + split;
+  const int k_end_g = min(key_end_of(min(NW * tgi + NW - 1, n_mt - 1)), k_begin + split_len);   // the workgroup's
+  const int mt = NW * tgi + wave;                          // this wave's tile
+  const bool tile_ok = mt < n_mt;
+  const int R = mt * 16 + col;
+  const bool row_ok = tile_ok && R < n_rows;
+  const int i_row = T - Tq + (row_ok ? R / G : 0);         // the row's token, as a local index
+  const int i_first = T - Tq + (mt * 16) / G;              // the tile's first token
+  const int k_end = tile_ok ? min(key_end_of(mt), k_begin + split_len) : k_begin;
+  // keys below k_full are seen by every row of the tile: memory, and local
+  // keys up to the tile's first token
+  const int k_full = min(k_end, M + max(0, i_first + 1));
 
-  if (tid < HALF) omega[tid] = exp2(-(2.0 * tid / D) * log2_theta);
-  u32x4 qraw[KS];
-  {
-    const uint16_t *src = q + (((int64_t)b * Tq + t_row) * Hq + g * G + (row_ok ? R % G : 0)) * D + 8 * grp;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qraw[s] = ld16(src + 32 * s);
-  }
-
-  // cooperative loads of the 16-key group at kb (keys past the workgroup's
-  // range read its last key; every wave masks them)
+  // Cooperative loads of the 64-key group at kb (keys past the workgroup's
+  // range read its last key; every wave masks them).  K piece p of this
+  // thread: key (tid + p NTH) / (D/8), 16-byte chunk (tid + p NTH) % (D/8);
+  // V piece p: keys 4 qd .. +3 and dims 2 dp, 2 dp + 1 of
+  // (qd, dp) = ((tid + p NTH) / (D/2), (tid + p NTH) % (D/2)).
   const uint32_t mrow = 2u * Hkv * D, lrow = (uint32_t)Hkv * D;
+  const uint16_t *mem_b = mem_kv + (int64_t)b * mem_cap * mrow + (int64_t)g * D;
+  const uint16_t *lk_b = local_k + (int64_t)b * local_cap * lrow + (int64_t)g * D;
+  const uint16_t *lv_b = local_v + (int64_t)b * local_cap * lrow + (int64_t)g * D;
   auto key_k = [&](int k) -> const uint16_t * {
-    return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mrow + (int64_t)g * D
-                 : local_k + ((int64_t)b * local_cap + (k - M)) * lrow + (int64_t)g * D;
+    return k < M ? mem_b + (int64_t)k * mrow : lk_b + (int64_t)(k - M) * lrow;
   };
   auto key_v = [&](int k) -> const uint16_t * {
-    return k < M ? mem_kv + ((int64_t)b * mem_cap + k) * mrow + lrow + (int64_t)g * D
-                 : local_v + ((int64_t)b * local_cap + (k - M)) * lrow + (int64_t)g * D;
+    return k < M ? mem_b + (int64_t)k * mrow + lrow : lv_b + (int64_t)(k - M) * lrow;
   };
-  const int kk = tid / (D / 8), ch = tid % (D / 8);        // K: key, 16-byte piece
-  const int qd = tid / (D / 2), dp = tid % (D / 2);        // V: key quad, dim pair
-  u32x4 kreg = {0u, 0u, 0u, 0u};
-  uint32_t vreg[4] = {0u, 0u, 0u, 0u};
+  u32x4 kreg[KPT];
+  uint32_t vreg[VPT][4];
   auto gload = [&](int kb) {
-    if (KT >= NTH || tid < KT) kreg = ld16(key_k(min(kb + kk, k_end_g - 1)) + 8 * ch);
-    if (VT >= NTH || tid < VT) {
+    const bool in_mem = kb + KG <= M, in_loc = kb >= M;   // (uniform)
+    if (kb + KG <= k_end_g && (in_mem || in_loc)) {
+      // the whole group in one array and in range: one base (scalar), one
+      // row stride, 32-bit byte offsets per lane
+      const uint32_t stride = in_mem ? mrow : lrow;
+      const char *kbase = reinterpret_cast<const char *>(in_mem ? mem_b + (int64_t)kb * mrow
+                                                                : lk_b + (int64_t)(kb - M) * lrow);
+      const char *vbase = reinterpret_cast<const char *>(in_mem ? mem_b + (int64_t)kb * mrow + lrow
+                                                                : lv_b + (int64_t)(kb - M) * lrow);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vreg[i] = *reinterpret_cast<const uint32_t *>(key_v(min(kb + 4 * qd + i, k_end_g - 1)) + 2 * dp);
+      for (int p = 0; p < KPT; ++p) {
+        const int i = tid + p * NTH;
+        if (KPN >= NTH || i < KPN)
+          kreg[p] = ld16(kbase + 2u * ((uint32_t)(i / (D / 8)) * stride + 8u * (uint32_t)(i % (D / 8))));
+      }
+#pragma unroll
+      for (int p = 0; p < VPT; ++p) {
+        const int i = tid + p * NTH, qd = i / (D / 2), dp = i % (D / 2);
+        if (VPN >= NTH || i < VPN) {
+          const uint32_t off = 2u * ((uint32_t)(4 * qd) * stride + 2u * (uint32_t)dp);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vreg[p][e] = *reinterpret_cast<const uint32_t *>(vbase + (size_t)(2u * e * stride) + off);
+        }
+      }
+      return;
+    }
+    // a group across the boundary or past the range (keys past it read the last one)
+#pragma unroll
+    for (int p = 0; p < KPT; ++p) {
+      const int i = tid + p * NTH;
+      if (KPN >= NTH || i < KPN) kreg[p] = ld16(key_k(min(kb + i / (D / 8), k_end_g - 1)) + 8 * (i % (D / 8)));
+    }
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) {
+      const int i = tid + p * NTH, qd = i / (D / 2), dp = i % (D / 2);
+      if (VPN >= NTH || i < VPN) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vreg[p][e] = *reinterpret_cast<const uint32_t *>(key_v(min(kb + 4 * qd + e, k_end_g - 1)) + 2 * dp);
+      }
     }
   };
   auto lstore = [&](int buf) {
-    if (KT >= NTH || tid < KT) st16(&ks[buf][kk * KRS + 8 * ch], kreg);
-    if (VT >= NTH || tid < VT) {
-      u32x2 lo, hi;                                        // dims 2dp and 2dp+1 of keys 4qd .. 4qd+3
-      lo.x = (vreg[0] & 0xffffu) | (vreg[1] << 16);
-      lo.y = (vreg[2] & 0xffffu) | (vreg[3] << 16);
-      hi.x = (vreg[0] >> 16) | (vreg[1] & 0xffff0000u);
-      hi.y = (vreg[2] >> 16) | (vreg[3] & 0xffff0000u);
-      *reinterpret_cast<u32x2 *>(&vt[buf][(2 * dp) * VTS + 4 * qd]) = lo;
-      *reinterpret_cast<u32x2 *>(&vt[buf][(2 * dp + 1) * VTS + 4 * qd]) = hi;
+#pragma unroll
+    for (int p = 0; p < KPT; ++p) {
+      const int i = tid + p * NTH;
+      if (KPN >= NTH || i < KPN) st16(&ks[buf][(i / (D / 8)) * KRS + 8 * (i % (D / 8))], kreg[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) {
+      const int i = tid + p * NTH, qd = i / (D / 2), dp = i % (D / 2);
+      if (VPN < NTH && i >= VPN) continue;
+      // keys 4 qd .. 4 qd + 3: half qd / 8, slots from 8 (qd % 4) + 4 ((qd / 4) % 2)
+      const int hv = qd >> 3, sb = 8 * (qd & 3) + 4 * ((qd >> 2) & 1);
+      u32x2 lo, hi;                                        // dims 2dp and 2dp+1 of the four keys
+      lo.x = (vreg[p][0] & 0xffffu) | (vreg[p][1] << 16);
+      lo.y = (vreg[p][2] & 0xffffu) | (vreg[p][3] << 16);
+      hi.x = (vreg[p][0] >> 16) | (vreg[p][1] & 0xffff0000u);
+      hi.y = (vreg[p][2] >> 16) | (vreg[p][3] & 0xffff0000u);
+      *reinterpret_cast<u32x2 *>(&vt[buf][hv][(2 * dp) * VRS + sb]) = lo;
+      *reinterpret_cast<u32x2 *>(&vt[buf][hv][(2 * dp + 1) * VRS + sb]) = hi;
     }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;                    // l_run: this lane's part of the sum
   f32x4 acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 qhi[KS], qlo[KS];
+  int buf = 0;
+
+  // S^T for quarter j of the staged group
+  auto s_quarter = [&](int j, f32x4 &sc) {
+    sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 kv8 = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(&ks[buf][(16 * j + col) * KRS + 32 * s + 8 * grp]));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qhi[s]), sc, 0, 0, 0);
+      if (MSA_ATT_BLOCK_QLO)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qlo[s]), sc, 0, 0, 0);
+    }
+  };
+  // online softmax of a half's 8 scores per lane: raises the running max if
+  // due (the factor for the accumulators in corr; raise: some lane must
+  // apply it) and returns P^T for the half
+  auto softmax = [&](const f32x4 &s0, const f32x4 &s1, float &corr, bool &raise) -> u32x4 {
+    const float mx = col_max4(fmaxf(amax4(s0), amax4(s1)));
+    raise = mx > m_run + kALazy;                           // (true for the first finite score)
+    corr = raise ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;   // (0 while nothing was seen)
+    m_run = raise ? mx : m_run;
+    l_run *= corr;
+    // scores -inf (masked) weigh 0, also while no score was finite
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float pr[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f((i < 4 ? s0[i] : s1[i - 4]) - m_use);
+      psum += pr[i];
+    }
+    l_run += psum;
+    return u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
+                 pack_bf16x2(pr[6], pr[7])};
+  };
+  // the accumulators hold O^T: this lane's column is its query, so the
+  // factor is the lane's own (exactly 1 where the max was kept)
+  auto rescale = [&](float corr, bool raise) {
+    if (__any(raise)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[nt][rr] *= corr;
+    }
+  };
+  // O^T += V^T P^T for half h: k-slot 8 grp + i is key 4 grp + i of quarter
+  // 2h (i < 4) or of quarter 2h + 1 (i >= 4), for V^T and P^T alike (a
+  // quarter past the tile's keys has weights 0 and finite staged values)
+  auto pv = [&](int h, const u32x4 &pp) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const bf16x8 vv = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4 *>(&vt[buf][h][(16 * nt + col) * VRS + 8 * grp]));
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, __builtin_bit_cast(bf16x8, pp), acc[nt], 0, 0, 0);
+    }
+  };
+  // mask: keys out of the tile's range, local keys after the row's token
+  auto mask = [&](int kj, f32x4 &sc) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int key = kj + 4 * grp + rr;
+      const bool ok = row_ok && key < k_end && (key < M || key - M <= i_row);
+      sc[rr] = ok ? sc[rr] : -INFINITY;
+    }
+  };
 
   if (k_begin < k_end_g) {                                 // (uniform over the workgroup)
     gload(k_begin);
-    lstore(0);
-    __syncthreads();                                       // the first group and omega
-    // rotated, scaled query as B-operand fragments (hi + lo bf16)
-    u32x4 qhi[KS], qlo[KS];
+    // the query rows (rotated and scaled by the pre-pass, fp32) as B-operand
+    // fragments (hi + lo bf16); the loads overlap the first group's
     {
-      float x[KS][8];
+      const float4 *src = reinterpret_cast<const float4 *>(
+          rot_q + (((int64_t)b * Tq + (row_ok ? R / G : 0)) * Hq + g * G + (row_ok ? R % G : 0)) * D + 8 * grp);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        float f[8];
-        Elt<uint16_t>::unpack(qraw[s], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[s][e] = row_ok ? f[e] : 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < HS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float c, sn;
-          rope_phasor((double)o + (double)i_row, omega[32 * s + 8 * grp + e], &c, &sn);
-          const float x1 = x[s][e], x2 = x[s + HS][e];
-          x[s][e] = (x1 * c - x2 * sn) * scale_log2;
-          x[s + HS][e] = (x2 * c + x1 * sn) * scale_log2;
-        }
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
+        const float4 x0 = src[8 * s], x1 = src[8 * s + 1];
+        const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         float hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          hi[e] = bf16_to_f32(f32_to_bf16(x[s][e]));
-          lo[e] = x[s][e] - hi[e];
+          const float x = row_ok ? f[e] : 0.f;
+          hi[e] = bf16_to_f32(f32_to_bf16(x));
+          lo[e] = x - hi[e];
         }
         qhi[s] = Elt<uint16_t>::pack(hi);
         qlo[s] = Elt<uint16_t>::pack(lo);
       }
     }
-    int buf = 0;
-    for (int kb = k_begin; kb < k_end_g; kb += 16) {
-      const bool more = kb + 16 < k_end_g;                 // (uniform)
-      if (more) gload(kb + 16);
-      // S^T = K Q^T: lane l holds S[row l%16][keys 4(l/16) .. +4]
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    lstore(0);
+    __syncthreads();                                       // the first group in place
+    for (int kb = k_begin; kb < k_end_g; kb += KG) {
+      const bool more = kb + KG < k_end_g;                 // (uniform)
+      if (more) gload(kb + KG);
+      // quarters of this group the tile sees (keys kb + 16 j .. below k_end)
+      const int nq = min(4, max(0, (k_end - kb + 15) >> 4));   // (uniform over the wave)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kv8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
-                                                          &ks[buf][col * KRS + 32 * s + 8 * grp]));
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qhi[s]), sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, __builtin_bit_cast(bf16x8, qlo[s]), sc, 0, 0, 0);
-      }
-      if (!(kb + 15 < k_end && kb + 15 - M <= i_first)) {
+      for (int h = 0; h < 2; ++h) {
+        if (2 * h >= nq) continue;                        // (uniform) no key of this half is seen
+        f32x4 sc[2];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int key = kb + 4 * grp + rr;
-          const bool ok = row_ok && key < k_end && (key < M || key - M <= i_row);
-          sc[rr] = ok ? sc[rr] : -INFINITY;
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * h + jj;
+          if (j < nq) {
+            s_quarter(j, sc[jj]);
+            if (!(kb + 16 * j + 15 < k_full)) mask(kb + 16 * j, sc[jj]);
+          } else {
+            sc[jj] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          }
         }
-      }
-      float mt_ = amax4(sc);
-      mt_ = fmaxf(mt_, __shfl_xor(mt_, 16, 64));
-      mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, 64));
-      const float m_new = fmaxf(m_run, mt_);
-      const bool none = m_new == -INFINITY;
-      const float corr = none ? 1.f : exp2f(m_run - m_new);
-      float psum = 0.f;
-      s16x4 pa;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float pr = none ? 0.f : exp2f(sc[rr] - m_new);
-        psum += pr;
-        pa[rr] = (short)f32_to_bf16(pr);
-      }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * corr + psum;
-      if (__any(m_new > m_run)) {
-        float cr[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) cr[rr] = __shfl(corr, 4 * grp + rr, 64);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) acc[nt][rr] *= cr[rr];
-      }
-      m_run = m_new;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const u32x2 vb = *reinterpret_cast<const u32x2 *>(&vt[buf][(16 * nt + col) * VTS + 4 * grp]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, vb), acc[nt], 0, 0, 0);
+        float corr;
+        bool raise;
+        const u32x4 pp = softmax(sc[0], sc[1], corr, raise);
+        rescale(corr, raise);
+        pv(h, pp);
       }
       if (more) lstore(buf ^ 1);
       __syncthreads();                                     // next group in place; this one free
       buf ^= 1;
     }
   }
-  if (!tile_ok) return;
 
-  // ---- partials: (m, l) from the S layout, acc from the O layout ----
-  if (grp == 0 && col < rps && row_ok) {
-    part_ml[2 * (slot * rps + col)] = m_run;
-    part_ml[2 * (slot * rps + col) + 1] = l_run;
-  }
+  // ---- partials: lane (col, grp) holds query row col of the tile: its
+  // (m, l) and dims 16 nt + 4 grp .. + 3 of its accumulator ----
+  if (!tile_ok) return;
+  const float l = col_sum4(l_run);
+  const int64_t slot = (((int64_t)b * Hkv + g) * n_mt + mt) * n_split + split;
+  if (col < rps && row_ok) {
+    if (grp == 0) *reinterpret_cast<float2 *>(part_ml + 2 * (slot * rps + col)) = float2{m_run, l};
+    float *dst = part_acc + (slot * rps + col) * D + 4 * grp;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = 4 * grp + rr;
-    if (row < rps && mt * 16 + row < n_rows) {
-      float *dst = part_acc + (slot * rps + row) * D + col;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = acc[nt][rr];
-    }
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<float4 *>(dst + 16 * nt) = float4{acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]};
   }
 }
 
-// Local keys rotated once to their positions o + i (i < local_len), for
-// launches in which several query tiles per KV head read every key: thread
-// per (query, token, KV head, 8 pairs), the phasor of each pair evaluated
-// exactly (angle reduced in fp64).
+// The pre-pass of launches in which several query tiles per KV head read
+// every key (prefill): the local keys rotated once to their positions o + i
+// (i < local_len), and the query block rotated to its tokens' positions
+// o + T - Tq + t and scaled (scale * log2 e, as the kernels use it) into
+// fp32, so the attention kernels rotate nothing.  Thread per (row, 8 pairs):
+// key rows first, then query rows; each phasor is evaluated exactly (angle
+// reduced in fp64), the frequencies come from a per-workgroup table.
 template <int D>
-__global__ __launch_bounds__(256) void rope_local_kernel(const uint16_t *__restrict__ local_k,
-                                                         const int32_t *__restrict__ local_len,
-                                                         const int32_t *__restrict__ pos_offset,
-                                                         uint16_t *__restrict__ rot_k, int B, int Hkv, int local_cap,
-                                                         double log2_theta) {
+__global__ __launch_bounds__(256) void rope_prepass_kernel(const uint16_t *__restrict__ local_k,
+                                                           const uint16_t *__restrict__ q,
+                                                           const int32_t *__restrict__ local_len,
+                                                           const int32_t *__restrict__ pos_offset,
+                                                           uint16_t *__restrict__ rot_k, float *__restrict__ rot_q,
+                                                           int B, int Tq, int Hq, int Hkv, int local_cap,
+                                                           float scale_log2, double log2_theta) {
   constexpr int HALF = D / 2, NC = HALF / 8;              // 8-pair chunks per head
+  __shared__ double omega[HALF];
+  if (threadIdx.x < HALF) omega[threadIdx.x] = exp2(-(2.0 * threadIdx.x / D) * log2_theta);
+  __syncthreads();
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n = (int64_t)B * local_cap * Hkv * NC;
-  if (id >= n) return;
-  const int c = (int)(id % NC);
-  const int64_t row = id / NC;                             // (b * local_cap + i) * Hkv + g
-  const int64_t bi = row / Hkv;
-  const int b = (int)(bi / local_cap), i = (int)(bi % local_cap);
+  const int64_t n_k = (int64_t)B * local_cap * Hkv * NC;
+  const int64_t n_q = (int64_t)B * Tq * Hq * NC;
+  if (id >= n_k + n_q) return;
+  const bool key = id < n_k;
+  const int64_t idx = key ? id : id - n_k;
+  const int c = (int)(idx % NC);
+  const int64_t row = idx / NC;                            // key: (b * local_cap + i) * Hkv + g; query: (b * Tq + t) * Hq + h
+  const int64_t bt = row / (key ? Hkv : Hq);
+  const int b = (int)(bt / (key ? local_cap : Tq)), it = (int)(bt % (key ? local_cap : Tq));
   const int T = max(0, min(local_len[b], local_cap));
-  if (i >= T) return;                                      // never read
-  const double pos = (double)pos_offset[b] + (double)i;
-  const uint16_t *src = local_k + row * D + 8 * c;
+  if (key && it >= T) return;                              // never read
+  const double pos = (double)pos_offset[b] + (double)(key ? it : T - Tq + it);
+  const uint16_t *src = (key ? local_k : q) + row * D + 8 * c;
   float a[8], z[8], r1[8], r2[8];
   Elt<uint16_t>::unpack(ld16(src), a);
   Elt<uint16_t>::unpack(ld16(src + HALF), z);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int j = 8 * c + e;
     float cs, sn;
-    rope_phasor(pos, exp2(-(2.0 * j / D) * log2_theta), &cs, &sn);
+    rope_phasor(pos, omega[8 * c + e], &cs, &sn);
     r1[e] = a[e] * cs - z[e] * sn;
     r2[e] = z[e] * cs + a[e] * sn;
   }
-  uint16_t *dst = rot_k + row * D + 8 * c;
-  st16(dst, Elt<uint16_t>::pack(r1));
-  st16(dst + HALF, Elt<uint16_t>::pack(r2));
+  if (key) {
+    uint16_t *dst = rot_k + row * D + 8 * c;
+    st16(dst, Elt<uint16_t>::pack(r1));
+    st16(dst + HALF, Elt<uint16_t>::pack(r2));
+  } else {
+    float4 *dst = reinterpret_cast<float4 *>(rot_q + row * D + 8 * c);
+    dst[0] = make_float4(r1[0] * scale_log2, r1[1] * scale_log2, r1[2] * scale_log2, r1[3] * scale_log2);
+    dst[1] = make_float4(r1[4] * scale_log2, r1[5] * scale_log2, r1[6] * scale_log2, r1[7] * scale_log2);
+    dst += HALF / 4;
+    dst[0] = make_float4(r2[0] * scale_log2, r2[1] * scale_log2, r2[2] * scale_log2, r2[3] * scale_log2);
+    dst[1] = make_float4(r2[4] * scale_log2, r2[5] * scale_log2, r2[6] * scale_log2, r2[7] * scale_log2);
+  }
 }
 
 // Combine the splits of one output row (b, t, h).  Wave 0 forms the
@@ -821,17 +955,37 @@ __global__ __launch_bounds__(kAWaves * 64) void attend_merge_wave_kernel(
 
 }  // namespace
 
+// Waves (query tiles) per workgroup of the block kernel: as many as there
+// are tiles per KV head, up to 16.
+static int block_waves(int n_mt) {
+  return n_mt >= 16 && MSA_ATT_BLOCK_NWMAX >= 16 ? 16 : n_mt >= 8 && MSA_ATT_BLOCK_NWMAX >= 8 ? 8 : 4;
+}
+
 // Keys per split: enough work items (waves) to give every CU about 16, in
 // whole 64-key blocks, between 64 and 512 keys.  Sized from the capacities,
-// which the host knows; splits past a tile's visible keys exit at once.
+// which the host knows; splits past a tile's visible keys exit at once.  The
+// block kernel (prefill) counts its workgroups of NW tiles instead and cuts
+// the keys into whole 16-key quarters, so that the workgroups fill the CUs.
 void attend_plan(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t mem_cap, int32_t local_cap,
                  AttendPlan *p) {
   const int G = hq / hkv;
   p->n_mt = (q_tokens * G + 15) / 16;
   p->rps = std::min(16, q_tokens * G);
   const int64_t total = std::max<int64_t>(1, (int64_t)mem_cap + local_cap);
-  const int64_t tiles = (int64_t)batch * hkv * p->n_mt;
   const int64_t want = (int64_t)device_info().n_cu * MSA_ATT_WAVES_PER_CU;
+  if (MSA_ATT_PREROT && MSA_ATT_BLOCK && p->n_mt >= 4) {
+    const int nw = block_waves(p->n_mt);
+    const int64_t wgs = (int64_t)batch * hkv * ((p->n_mt + nw - 1) / nw);   // workgroups per split
+    // as many waves as the CUs hold at the kernel's register budget
+    const int64_t want_b = (int64_t)device_info().n_cu * std::max(nw, MSA_ATT_BLOCK_WAVES);
+    const int64_t ns0 = std::max<int64_t>(1, std::min<int64_t>(kAMaxSplit, want_b / (wgs * nw)));
+    int64_t len = ((total + ns0 - 1) / ns0 + 15) / 16 * 16;
+    len = std::max<int64_t>(64, std::min<int64_t>(MSA_ATT_SPLIT_MAX, len));
+    p->split_len = (int)len;
+    p->n_split = (int)std::min<int64_t>(kAMaxSplit, (total + len - 1) / len);
+    return;
+  }
+  const int64_t tiles = (int64_t)batch * hkv * p->n_mt;
   int64_t len = (total * tiles + want - 1) / want;
   len = std::max<int64_t>(64, std::min<int64_t>(MSA_ATT_SPLIT_MAX, ((len + 63) / 64) * 64));
   int64_t ns = (total + len - 1) / len;
@@ -851,29 +1005,31 @@ size_t attend_ws_layout(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv
   const size_t rows = (size_t)batch * hkv * p.n_mt * p.n_split * p.rps;
   const size_t o_ml = (sizeof(float) * rows * d + 255) & ~(size_t)255;
   const size_t o_rk = (o_ml + sizeof(float) * 2 * rows + 255) & ~(size_t)255;
-  // several query tiles per KV head read every local key: rotate them once
+  // several query tiles per KV head read every local key: rotate the keys
+  // (bf16) and the query block (fp32) once
   const bool prerot = p.n_mt > 1;
-  const size_t end = prerot ? (o_rk + sizeof(uint16_t) * (size_t)batch * local_cap * hkv * d + 255) & ~(size_t)255
-                            : o_rk;
+  const size_t o_rq = (o_rk + sizeof(uint16_t) * (size_t)batch * local_cap * hkv * d + 255) & ~(size_t)255;
+  const size_t end = prerot ? (o_rq + sizeof(float) * (size_t)batch * q_tokens * hq * d + 255) & ~(size_t)255 : o_rk;
   if (base) {
     ws->part_acc = reinterpret_cast<float *>(base);
     ws->part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(base) + o_ml);
     ws->rot_k = prerot ? reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(base) + o_rk) : nullptr;
+    ws->rot_q = prerot ? reinterpret_cast<float *>(reinterpret_cast<char *>(base) + o_rq) : nullptr;
   }
   return end;
 }
 
 template <int D, int NW>
 static hipError_t launch_block(const msa_attend_args &a, const AttendPlan &p, const AttendWs &ws, const uint16_t *lk,
-                               float scale, hipStream_t s) {
+                               hipStream_t s) {
   const int64_t n_wg = (int64_t)a.n_kv_heads * a.batch * ((p.n_mt + NW - 1) / NW) * p.n_split;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   hipExtLaunchKernelGGL((attend_block_kernel<D, NW>), dim3((unsigned)n_wg), dim3(NW * 64), 0, s,
                         prof_event(a.prof_event_begin), prof_event(a.prof_event_end), 0,
-                        reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
-                        a.mem_len, lk, reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset,
-                        ws.part_acc, ws.part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap,
-                        a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
+                        reinterpret_cast<const uint16_t *>(a.mem_kv), a.mem_len, lk,
+                        reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, ws.part_acc, ws.part_ml, a.batch,
+                        a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap, a.local_cap, p.n_mt, p.n_split,
+                        p.split_len, p.rps, ws.rot_q);
   return hipGetLastError();
 }
 
@@ -889,18 +1045,22 @@ static hipError_t launch_attend_t(const msa_attend_args &a, const AttendWs &ws, 
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
   const uint16_t *lk = reinterpret_cast<const uint16_t *>(a.local_k);
-  if (PREROT && lk) {
-    const int64_t n = (int64_t)a.batch * a.local_cap * a.n_kv_heads * (D / 16);
-    hipLaunchKernelGGL((rope_local_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, lk, a.local_len,
-                       a.pos_offset, ws.rot_k, a.batch, a.n_kv_heads, a.local_cap, log2(a.rope_theta));
+  if (PREROT) {
+    const int64_t n = ((int64_t)a.batch * a.local_cap * a.n_kv_heads + (int64_t)a.batch * a.q_tokens * a.n_q_heads) *
+                      (D / 16);
+    hipLaunchKernelGGL((rope_prepass_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, lk,
+                       reinterpret_cast<const uint16_t *>(a.q), a.local_len, a.pos_offset, ws.rot_k, ws.rot_q,
+                       a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, lk ? a.local_cap : 0, scale * kALog2e,
+                       log2(a.rope_theta));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    lk = ws.rot_k;
+    if (lk) lk = ws.rot_k;
   }
   if (PREROT && MSA_ATT_BLOCK && p.n_mt >= 4) {
     // as many query tiles per workgroup as there are, up to 16
-    e = p.n_mt >= 16 ? launch_block<D, 16>(a, p, ws, lk, scale, s)
-        : p.n_mt >= 8 ? launch_block<D, 8>(a, p, ws, lk, scale, s)
-                      : launch_block<D, 4>(a, p, ws, lk, scale, s);
+    const int nw = block_waves(p.n_mt);
+    e = nw == 16 ? launch_block<D, 16>(a, p, ws, lk, s)
+        : nw == 8 ? launch_block<D, 8>(a, p, ws, lk, s)
+                  : launch_block<D, 4>(a, p, ws, lk, s);
     if (e != hipSuccess) return e;
   } else {
     hipExtLaunchKernelGGL((attend_kernel<D, PREROT>), dim3((unsigned)grid), dim3(kAWaves * 64), 0, s,
@@ -908,7 +1068,8 @@ static hipError_t launch_attend_t(const msa_attend_args &a, const AttendWs &ws, 
                           reinterpret_cast<const uint16_t *>(a.q), reinterpret_cast<const uint16_t *>(a.mem_kv),
                           a.mem_len, lk, reinterpret_cast<const uint16_t *>(a.local_v), a.local_len, a.pos_offset,
                           ws.part_acc, ws.part_ml, a.batch, a.q_tokens, a.n_q_heads, a.n_kv_heads, a.mem_cap,
-                          a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta));
+                          a.local_cap, p.n_mt, p.n_split, p.split_len, p.rps, scale * kALog2e, log2(a.rope_theta),
+                          ws.rot_q);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int64_t rows = (int64_t)a.batch * a.q_tokens * a.n_q_heads;

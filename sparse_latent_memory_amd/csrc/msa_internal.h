@@ -162,12 +162,14 @@ struct AttendPlan {
 };
 void attend_plan(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t mem_cap, int32_t local_cap,
                  AttendPlan *p);
-// Attention workspace: split partials, and the local keys rotated once when
-// several query tiles per KV head read them (else rot_k is null).
+// Attention workspace: split partials, and the local keys and the query
+// block rotated once when several query tiles per KV head read them (else
+// rot_k and rot_q are null).
 struct AttendWs {
   float *part_acc;
   float *part_ml;
   uint16_t *rot_k;         // [B, local_cap, Hkv, D] bf16 or null
+  float *rot_q;            // [B, Tq, Hq, D] fp32, rotated and scaled, or null (with rot_k)
 };
 size_t attend_ws_layout(int32_t batch, int32_t q_tokens, int32_t hq, int32_t hkv, int32_t d, int32_t mem_cap,
                         int32_t local_cap, void *base, AttendWs *ws);
