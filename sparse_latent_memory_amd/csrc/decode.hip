@@ -76,10 +76,14 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 2 : 3) void dec
   auto slot = [&](int hh) { return ((int64_t)b * Hq + g * G + hh) * n_split + split; };
 
   if (k0 >= k1) {
+    // an empty split: weight 0 in the merge, and finite zeros where the
+    // merge reads its accumulator (0 times stale workspace contents could
+    // be NaN)
     for (int hh = threadIdx.x; hh < G; hh += blockDim.x) {
       part_ml[2 * slot(hh)] = -INFINITY;
       part_ml[2 * slot(hh) + 1] = 0.f;
     }
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) part_acc[slot(i / D) * D + i % D] = 0.f;
     return;
   }
 

@@ -112,6 +112,7 @@ def check_topk_order(idx_gpu, score_gpu, what=""):
 def check_decode(got, ref, dtype, what=""):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    assert np.array_equal(np.isfinite(got), np.isfinite(ref)), f"{what}: non-finite values where the reference has none"
     err = np.linalg.norm(got - ref, axis=-1)
     lim = DECODE_REL[dtype] * np.linalg.norm(ref, axis=-1) + 1e-6
     bad = err > lim
