@@ -90,15 +90,29 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(
   const int M = B * Tq;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
-  for (int mh = wave; mh < M * HR; mh += kWaves) {
-    const uint16_t *src = qr + (int64_t)mh * DR;
+  // 1 / (|q| Hr) per (token, head): four threads per (token, head), each
+  // summing a quarter of the head's squares, with all of a thread's loads
+  // in flight at once (at most 8 tokens x 8 heads: one pass)
+  static_assert(DR % 32 == 0, "router head dim a multiple of 32");
+  for (int base = 0; base < M * HR; base += 64) {
+    const int mh = base + (threadIdx.x >> 2), part = threadIdx.x & 3;
     float ss = 0.f;
-    for (int i = lane; i < DR; i += 64) {
-      const float x = bf16_to_f32(src[i]);
-      ss += x * x;
+    if (mh < M * HR) {
+      const uint16_t *src = qr + (int64_t)mh * DR + part * (DR / 4);
+      u32x4 v[DR / 32];
+#pragma unroll
+      for (int i = 0; i < DR / 32; ++i) v[i] = ld16(src + 8 * i);
+#pragma unroll
+      for (int i = 0; i < DR / 32; ++i) {
+        float x[8];
+        Elt<uint16_t>::unpack(v[i], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      }
     }
-    ss = wave_sum(ss);
-    if (lane == 0) qscale[mh] = 1.0f / (fmaxf(sqrtf(ss), kEps) * (float)HR);
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if (part == 0 && mh < M * HR) qscale[mh] = 1.0f / (fmaxf(sqrtf(ss), kEps) * (float)HR);
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < NF * 64; idx += blockDim.x) {
@@ -107,13 +121,14 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(
     const int r = l & 15, m = r >> 1;
     uint32_t w[4] = {0, 0, 0, 0};
     if (m < M) {
-      const uint16_t *src = qr + ((int64_t)m * HR + h) * DR + 32 * s + 8 * (l >> 4);
+      float x[8];
+      Elt<uint16_t>::unpack(ld16(qr + ((int64_t)m * HR + h) * DR + 32 * s + 8 * (l >> 4)), x);
       const float sc = qscale[m * HR + h];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = bf16_to_f32(src[e]) * sc;
-        const uint16_t hi = f32_to_bf16(x);
-        const uint16_t val = (r & 1) ? f32_to_bf16(x - bf16_to_f32(hi)) : hi;
+        const float y = x[e] * sc;
+        const uint16_t hi = f32_to_bf16(y);
+        const uint16_t val = (r & 1) ? f32_to_bf16(y - bf16_to_f32(hi)) : hi;
         w[e >> 1] |= (uint32_t)val << (16 * (e & 1));
       }
     }
