@@ -102,25 +102,6 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ float amax4(const f32x4 &v) { return fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])); }
 
-// x combined over the lanes l, l ^ 16, l ^ 32 and l ^ 48 - the four lanes
-// that hold one column of a 16x16 matrix-core result - with gfx950's lane
-// swaps (v_permlane32_swap exchanges the upper half of one operand with the
-// lower half of the other, v_permlane16_swap odd 16-lane rows with even
-// ones; given the same value twice, the two results hold x of lane l and of
-// lane l ^ 32, resp. l ^ 16, in every lane): VALU only, no LDS round trip.
-__device__ __forceinline__ float col_max4(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float col_sum4(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // bf16 number e (0..7) of a 16-byte vector
 __device__ __forceinline__ uint32_t bf16_at(const u32x4 &v, int e) {
   const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;

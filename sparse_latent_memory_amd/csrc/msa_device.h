@@ -96,6 +96,25 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// x combined over the lanes l, l ^ 16, l ^ 32 and l ^ 48 - the four lanes
+// that hold one column of a 16x16 matrix-core result - with gfx950's lane
+// swaps (v_permlane32_swap exchanges the upper half of one operand with the
+// lower half of the other, v_permlane16_swap odd 16-lane rows with even
+// ones; given the same value twice, the two results hold x of lane l and of
+// lane l ^ 32, resp. l ^ 16, in every lane): VALU only, no LDS round trip.
+__device__ __forceinline__ float col_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);

@@ -289,11 +289,12 @@ def test_route_many_tokens_matrix_core_path(hr, dr, b, tq):
     _route_check(kr, off, qr, 8, f"wide {hr}x{dr} B{b} Tq{tq}")
 
 
-@pytest.mark.parametrize("b,tq", [(257, 64), (65, 256)])
+@pytest.mark.parametrize("b,tq", [(257, 64), (65, 256), (129, 256)])
 def test_route_more_query_chunks_than_workgroups(b, tq):
     """More chunks of query tiles than workgroups (one per compute unit):
     each workgroup walks several chunks, restaging the query tiles between
-    them; with 256 tokens every query is also cut into partial maxima."""
+    them; with 256 tokens every query is also cut into partial maxima (four
+    chunks of four tiles per query: 260 and 516 chunks)."""
     g = torch.Generator().manual_seed(b + tq)
     kr, off = _ragged_bank(g, 100, 4, 8, 128, torch.bfloat16)
     qr = _randn(g, b, tq, 8, 128, dtype=torch.bfloat16).to(DEV)
@@ -611,7 +612,7 @@ def _route_both_layouts(qr, kr, off, k, what, pad_value=float("nan")):
 
 
 @pytest.mark.parametrize("hr,dr", [(8, 128), (4, 64), (1, 128), (16, 64), (2, 64)])
-@pytest.mark.parametrize("b,tq", [(1, 1), (3, 2), (8, 1), (16, 1), (2, 100)])
+@pytest.mark.parametrize("b,tq", [(1, 1), (3, 2), (8, 1), (16, 1), (2, 100), (1, 200)])
 def test_route_tiled_bank_matches_row_major(hr, dr, b, tq):
     """The tiled router bank gives the row-major bank's results bit for bit
     (narrow and wide scans), with NaN in the padding rows of its last tile;
