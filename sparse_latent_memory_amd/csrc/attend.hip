@@ -79,7 +79,7 @@ constexpr int kAMaxSplit = 4096;
 #ifndef MSA_ATT_BLOCK_NWMAX // largest number of query tiles (waves) per block-kernel workgroup: 4, 8 or 16
 #define MSA_ATT_BLOCK_NWMAX 16
 #endif
-#ifndef MSA_ATT_BLOCK_WAVES // waves per CU the block kernel's register budget aims for (one workgroup at least)
+#ifndef MSA_ATT_BLOCK_WAVES // waves per CU (4 SIMDs) the block kernel's register budget aims for
 #define MSA_ATT_BLOCK_WAVES 8
 #endif
 constexpr float kALog2e = 1.4426950408889634f;
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kAWaves * 64, 2) void attend_kernel(
 // whose tile lies past the last one loads and synchronises but stores
 // nothing.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, MSA_ATT_BLOCK_WAVES / NW > 0 ? MSA_ATT_BLOCK_WAVES / NW : 1) void attend_block_kernel(
+__global__ __launch_bounds__(NW * 64, MSA_ATT_BLOCK_WAVES / 4 > 0 ? MSA_ATT_BLOCK_WAVES / 4 : 1) void attend_block_kernel(
     const uint16_t *__restrict__ mem_kv, const int32_t *__restrict__ mem_len, const uint16_t *__restrict__ local_k,
     const uint16_t *__restrict__ local_v, const int32_t *__restrict__ local_len, float *__restrict__ part_acc,
     float *__restrict__ part_ml, int B, int Tq, int Hq, int Hkv, int mem_cap, int local_cap, int n_mt, int n_split,
