@@ -93,6 +93,22 @@ __global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict_
 // the MALL; workgroups are dispatched round-robin over the 8 XCDs, which the
 // XCD-major logical id below follows.
 constexpr int kWideWaves = 8;
+#ifndef MSA_WIDE_HEAD_OUTER // 1: heads outer when a workgroup walks few bank-tile groups (wide_tmax)
+#define MSA_WIDE_HEAD_OUTER 1
+#endif
+// Tiles per wave the heads-outer loop takes: as many (up to 4) as fit its
+// registers - a head's query fragments (4 NM KS), two bank fragments (8 KS),
+// 4 NM accumulators per tile and as many again for the epilogue - within a
+// budget of 160 (measured: no spills); 0: never.
+template <int NM, int KS>
+constexpr int wide_tmax() {
+  int t = 4;
+  while (t > 0 && 4 * NM * KS + 8 * KS + 4 * NM * (t + 1) > 160) --t;
+  return t;
+}
+#ifndef MSA_WIDE_STAGE_ROT // 1: workgroups staging the same query chunk start at different eighths of it
+#define MSA_WIDE_STAGE_ROT 1
+#endif
 
 // One doubling step of the segmented max over the 16 rows of a tile (lane
 // column = row): row r takes row r + SH's running max while no document
@@ -173,13 +189,13 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
   // One head of the tile: the query fragments are read from LDS in one batch
   // ahead of the MFMAs (the scheduling barrier keeps the compiler from
   // pairing each read with its MFMA), the Gram MFMAs covering their latency.
-  auto head = [&](int h, const u32x4 *f, f32x4 *acc) {
-    u32x4 a[NM][KS];
+  auto read_a = [&](int h, u32x4 (&a)[NM][KS]) {
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt)
 #pragma unroll
       for (int s = 0; s < KS; ++s) a[mt][s] = afrag[(mt * NF + h * KS + s) * 64 + lane];
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto head_mma = [&](const u32x4 (&a)[NM][KS], const u32x4 *f, f32x4 *acc) {
     f32x4 gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -203,6 +219,12 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
     const float inv = rsqrtf(fmaxf(__shfl(mine, diag_src, 64), kEps2));
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) acc[mt] += d[mt] * inv;
+  };
+  auto head = [&](int h, const u32x4 *f, f32x4 *acc) {
+    u32x4 a[NM][KS];
+    read_a(h, a);
+    __builtin_amdgcn_sched_barrier(0);
+    head_mma(a, f, acc);
   };
 
   // Document path (Tq == 1): lane (col, grp) holds, for bank row col of the
@@ -258,10 +280,74 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
     wide_chunk(L, c, &t0, &t1);
     const int nm = t1 - t0;
     __syncthreads();                    // readers of the previous chunk are done
-    for (int i = threadIdx.x; i < NM * NF * 64; i += blockDim.x)
-      afrag[i] = i < nm * NF * 64 ? frag[(int64_t)t0 * NF * 64 + i] : u32x4{0u, 0u, 0u, 0u};
+    {
+      // The workgroups of one XCD that stage the same chunk start at
+      // different eighths of it: each line is fetched from memory by one and
+      // found in L2 by the others, instead of all of them waiting on the same
+      // misses together.
+      constexpr int NTH = kWideWaves * 64, NIT = (NM * NF * 64 + NTH - 1) / NTH;
+      const int rot = MSA_WIDE_STAGE_ROT ? ((L.n_chunks <= nwg ? stream : 0) & 7) * NIT / 8 : 0;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int i = ((it + rot) % NIT) * NTH + (int)threadIdx.x;
+        if (i < NM * NF * 64) afrag[i] = i < nm * NF * 64 ? frag[(int64_t)t0 * NF * 64 + i] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
     __syncthreads();
     const int part = L.ppq > 1 ? c % L.ppq : 0;
+
+    // Few bank tiles per wave (a small bank, many query tiles): heads outer,
+    // so that a head's query fragments are read from LDS once and kept in
+    // registers for all of the wave's tiles, whose accumulators stay live;
+    // the per-head order of the sums is that of the tile loop below.
+    const int64_t n_my = stream < n_groups ? (n_groups - 1 - stream) / S + 1 : 0;   // groups this workgroup walks
+    constexpr int TM = wide_tmax<NM, KS>();
+    if constexpr (HR > 1 && MSA_WIDE_HEAD_OUTER && TM > 0) {
+      if (n_my <= TM) {
+      const int nj = (int)n_my;
+      f32x4 acc[TM][NM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      u32x4 fa[KS], fb[KS];
+      load(stream, 0, fa);
+#pragma unroll 1
+      for (int h = 0; h < HR; ++h) {
+        u32x4 a[NM][KS];
+        read_a(h, a);
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          if (j < nj) {                                  // (uniform)
+            // the next fragment: this head of the next tile, else the next
+            // head of the first (after the last head a valid, unused one)
+            const bool more = j + 1 < nj;
+            load(stream + (int64_t)(more ? j + 1 : 0) * S, more ? h : (h + 1 < HR ? h + 1 : 0), fb);
+            __builtin_amdgcn_sched_barrier(0);           // the prefetch stays ahead of the compute
+            head_mma(a, fa, acc[j]);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) fa[s] = fb[s];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        if (j < nj) {
+          const int64_t tile = (stream + (int64_t)j * S) * kWideWaves + wave;
+          const int64_t row = tile * 16 + col;
+          if (L.tok1) {
+            const int64_t tc = tile < n_tiles ? tile : n_tiles - 1;
+            const uint32_t bits = tile_bits[tc];
+            const int32_t tdoc = tile_doc[tc];
+            if (tile < n_tiles) epilogue_docs(t0, nm, tile, bits, tdoc, acc[j]);   // (wave-uniform)
+          } else if (row < n_pool) {
+            epilogue(t0, nm, part, row, acc[j]);
+          }
+        }
+      }
+      continue;
+      }
+    }
 
     u32x4 fa[KS], fb[KS];
     load(stream, 0, fa);
