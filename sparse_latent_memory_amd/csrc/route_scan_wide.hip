@@ -97,13 +97,14 @@ constexpr int kWideWaves = 8;
 #define MSA_WIDE_HEAD_OUTER 1
 #endif
 // Tiles per wave the heads-outer loop takes: as many (up to 4) as fit its
-// registers - a head's query fragments (4 NM KS), two bank fragments (8 KS),
-// 4 NM accumulators per tile and as many again for the epilogue - within a
-// budget of 160 (measured: no spills); 0: never.
+// registers - a head's query fragments (4 NM KS), per tile a bank-fragment
+// slot (4 KS) and 4 NM accumulators, and 4 NM more for the epilogue - within
+// a budget of 176 (measured: 2-4 registers spilled where the chunk holds 4
+// tiles of 8 heads x 128 dims, outside the matrix loops); 0: never.
 template <int NM, int KS>
 constexpr int wide_tmax() {
   int t = 4;
-  while (t > 0 && 4 * NM * KS + 8 * KS + 4 * NM * (t + 1) > 160) --t;
+  while (t > 0 && 4 * NM * KS + 4 * KS * t + 4 * NM * (t + 1) > 176) --t;
   return t;
 }
 #ifndef MSA_WIDE_STAGE_ROT // 1: workgroups staging the same query chunk start at different eighths of it
@@ -310,24 +311,24 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
       for (int j = 0; j < TM; ++j)
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      u32x4 fa[KS], fb[KS];
-      load(stream, 0, fa);
+      // one fragment slot per tile, refilled with the tile's next head as
+      // soon as it is used: TM loads in flight per wave.  No branches: slots
+      // past the workgroup's last group hold (clamped) fragments whose
+      // results are never stored, and the loads after the last head fetch a
+      // valid, unused one.
+      u32x4 fr[TM][KS];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) load(stream + (int64_t)j * S, 0, fr[j]);
 #pragma unroll 1
       for (int h = 0; h < HR; ++h) {
         u32x4 a[NM][KS];
         read_a(h, a);
+        const int hn = h + 1 < HR ? h + 1 : 0;
 #pragma unroll
         for (int j = 0; j < TM; ++j) {
-          if (j < nj) {                                  // (uniform)
-            // the next fragment: this head of the next tile, else the next
-            // head of the first (after the last head a valid, unused one)
-            const bool more = j + 1 < nj;
-            load(stream + (int64_t)(more ? j + 1 : 0) * S, more ? h : (h + 1 < HR ? h + 1 : 0), fb);
-            __builtin_amdgcn_sched_barrier(0);           // the prefetch stays ahead of the compute
-            head_mma(a, fa, acc[j]);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) fa[s] = fb[s];
-          }
+          __builtin_amdgcn_sched_barrier(0);
+          head_mma(a, fr[j], acc[j]);
+          load(stream + (int64_t)j * S, hn, fr[j]);
         }
       }
 #pragma unroll
