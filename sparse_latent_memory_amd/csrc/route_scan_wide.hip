@@ -96,14 +96,15 @@ constexpr int kWideWaves = 8;
 #ifndef MSA_WIDE_HEAD_OUTER // 1: heads outer when a workgroup walks few bank-tile groups (wide_tmax)
 #define MSA_WIDE_HEAD_OUTER 1
 #endif
-// Tiles per wave the heads-outer loop takes: as many (up to 4) as fit its
-// registers - a head's query fragments (4 NM KS), per tile a bank-fragment
-// slot (4 KS) and 4 NM accumulators, and 4 NM more for the epilogue - within
-// a budget of 176 (measured: 2-4 registers spilled where the chunk holds 4
-// tiles of 8 heads x 128 dims, outside the matrix loops); 0: never.
-template <int NM, int KS>
+// Tiles per wave the heads-outer loop takes: as many (up to 3; 2 with two
+// heads, whose loop is unrolled; 1 for chunks of 8 query tiles) as fit its
+// registers - a head's query fragments
+// (4 NM KS), per tile a bank-fragment slot (4 KS) and 4 NM accumulators, and
+// 4 NM more for the epilogue - within a budget of 176 (the caps and the
+// budget are where the compiled instantiations stop spilling); 0: never.
+template <int HR, int NM, int KS>
 constexpr int wide_tmax() {
-  int t = 4;
+  int t = NM >= 8 ? 1 : HR <= 2 ? 2 : 3;
   while (t > 0 && 4 * NM * KS + 4 * KS * t + 4 * NM * (t + 1) > 176) --t;
   return t;
 }
@@ -302,51 +303,58 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
     // registers for all of the wave's tiles, whose accumulators stay live;
     // the per-head order of the sums is that of the tile loop below.
     const int64_t n_my = stream < n_groups ? (n_groups - 1 - stream) / S + 1 : 0;   // groups this workgroup walks
-    constexpr int TM = wide_tmax<NM, KS>();
+    if (n_my == 0) continue;            // (uniform over the workgroup) no bank tile: nothing to stage or store
+    constexpr int TM = wide_tmax<HR, NM, KS>();
     if constexpr (HR > 1 && MSA_WIDE_HEAD_OUTER && TM > 0) {
       if (n_my <= TM) {
-      const int nj = (int)n_my;
-      f32x4 acc[TM][NM];
+        const int nj = (int)n_my;
+        f32x4 acc[TM][NM];
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
+        for (int j = 0; j < TM; ++j)
 #pragma unroll
-        for (int mt = 0; mt < NM; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // one fragment slot per tile, refilled with the tile's next head as
-      // soon as it is used: TM loads in flight per wave.  No branches: slots
-      // past the workgroup's last group hold (clamped) fragments whose
-      // results are never stored, and the loads after the last head fetch a
-      // valid, unused one.
-      u32x4 fr[TM][KS];
+          for (int mt = 0; mt < NM; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // one fragment slot per tile, refilled with the tile's next head as
+        // soon as it is used: TM loads in flight per wave.  No branches: slots
+        // past the workgroup's last group repeat the wave's last tile (its
+        // lines, already requested) and their results are never stored; the
+        // last head, peeled, loads nothing.
+        u32x4 fr[TM][KS];
+        auto gj = [&](int j) { return stream + (int64_t)max(0, min(j, nj - 1)) * S; };
 #pragma unroll
-      for (int j = 0; j < TM; ++j) load(stream + (int64_t)j * S, 0, fr[j]);
+        for (int j = 0; j < TM; ++j) load(gj(j), 0, fr[j]);
 #pragma unroll 1
-      for (int h = 0; h < HR; ++h) {
-        u32x4 a[NM][KS];
-        read_a(h, a);
-        const int hn = h + 1 < HR ? h + 1 : 0;
+        for (int h = 0; h < HR - 1; ++h) {
+          u32x4 a[NM][KS];
+          read_a(h, a);
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          __builtin_amdgcn_sched_barrier(0);
-          head_mma(a, fr[j], acc[j]);
-          load(stream + (int64_t)j * S, hn, fr[j]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (j < nj) {
-          const int64_t tile = (stream + (int64_t)j * S) * kWideWaves + wave;
-          const int64_t row = tile * 16 + col;
-          if (L.tok1) {
-            const int64_t tc = tile < n_tiles ? tile : n_tiles - 1;
-            const uint32_t bits = tile_bits[tc];
-            const int32_t tdoc = tile_doc[tc];
-            if (tile < n_tiles) epilogue_docs(t0, nm, tile, bits, tdoc, acc[j]);   // (wave-uniform)
-          } else if (row < n_pool) {
-            epilogue(t0, nm, part, row, acc[j]);
+          for (int j = 0; j < TM; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            head_mma(a, fr[j], acc[j]);
+            load(gj(j), h + 1, fr[j]);
           }
         }
-      }
-      continue;
+        {
+          u32x4 a[NM][KS];
+          read_a(HR - 1, a);
+#pragma unroll
+          for (int j = 0; j < TM; ++j) head_mma(a, fr[j], acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          if (j < nj) {
+            const int64_t tile = (stream + (int64_t)j * S) * kWideWaves + wave;
+            const int64_t row = tile * 16 + col;
+            if (L.tok1) {
+              const int64_t tc = tile < n_tiles ? tile : n_tiles - 1;
+              const uint32_t bits = tile_bits[tc];
+              const int32_t tdoc = tile_doc[tc];
+              if (tile < n_tiles) epilogue_docs(t0, nm, tile, bits, tdoc, acc[j]);   // (wave-uniform)
+            } else if (row < n_pool) {
+              epilogue(t0, nm, part, row, acc[j]);
+            }
+          }
+        }
+        continue;
       }
     }
 
