@@ -87,6 +87,11 @@ __global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict_
 // MFMAs against A-fragments read from LDS, scaled by the head's inverse norm.
 // Tiles of a chunk past its last real one are staged as zeros and their
 // results dropped, so the MFMA loop has no branches.
+// A workgroup that walks only a few groups of bank tiles (a small bank, many
+// query tiles: prefill routing) runs heads outer instead: each head's query
+// fragments are read from LDS once into registers and applied to all of the
+// wave's tiles, whose accumulators stay live, with one bank-fragment slot
+// per tile refilled as it is used.
 // When the query tiles span several chunks, chunks go to different
 // workgroups of one XCD that walk the same bank tiles in the same order, so
 // the bank is fetched from HBM about once and re-read from the XCD's L2 or
@@ -98,10 +103,10 @@ constexpr int kWideWaves = 8;
 #endif
 // Tiles per wave the heads-outer loop takes: as many (up to 3; 2 with two
 // heads, whose loop is unrolled; 1 for chunks of 8 query tiles) as fit its
-// registers - a head's query fragments
-// (4 NM KS), per tile a bank-fragment slot (4 KS) and 4 NM accumulators, and
-// 4 NM more for the epilogue - within a budget of 176 (the caps and the
-// budget are where the compiled instantiations stop spilling); 0: never.
+// registers - a head's query fragments (4 NM KS), per tile a bank-fragment
+// slot (4 KS) and 4 NM accumulators, and 4 NM more for the epilogue -
+// within a budget of 176 (the caps and the budget are where the compiled
+// instantiations stop spilling); 0: never.
 template <int HR, int NM, int KS>
 constexpr int wide_tmax() {
   int t = NM >= 8 ? 1 : HR <= 2 ? 2 : 3;
