@@ -312,20 +312,29 @@ def main():
     dec_ms = np.array([dec_ev.elapsed_ms(j) for j in range(len(samples))])
 
     # route + decode latency per step (synchronised each step), both assembly modes
+    # as a serving loop calls it (msa.RouteCall: every argument but the
+    # query bound once), and with route() marshalling all its arguments
+    calls = {name: msa.RouteCall(tuple(qrs[0].shape), qrs[0].dtype, bank, pool_off_d, k, doc_scores, topk_idx,
+                                 topk_score, rws, assembly=a, **rkw)
+             for name, a in (("kernel", asm), ("copies", asm_copies))}
     lat = {}
-    for name, a in (("kernel", asm), ("copies", asm_copies)):
+    for name, a, bound in (("kernel", asm, True), ("copies", asm_copies, True), ("kernel_route", asm, False)):
         vals = []
         for i in range(W + K, n_steps):
             torch.cuda.synchronize()
             t = time.perf_counter()
-            msa.route(qrs[i], bank, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=a, stream=stream,
-                      **rkw)
+            if bound:
+                calls[name](qrs[i], stream=stream)
+            else:
+                msa.route(qrs[i], bank, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=a,
+                          stream=stream, **rkw)
             msa.sparse_decode(qs[i], a.mem_kv, a.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
                               stream=stream)
             torch.cuda.synchronize()
             vals.append((time.perf_counter() - t) * 1e3)
         lat[name] = np.array(vals)
-    log(f"route+decode p50: kernel gather {np.median(lat['kernel']):.3f} ms, "
+    log(f"route+decode p50: kernel gather {np.median(lat['kernel']):.3f} ms "
+        f"(route() with every argument: {np.median(lat['kernel_route']):.3f} ms), "
         f"copy gather {np.median(lat['copies']):.3f} ms")
 
     # pipelined steady state: consecutive queries alternate between two
@@ -444,6 +453,7 @@ def main():
             "route_decode_p50": float(np.percentile(lat["kernel"], 50)),
             "route_decode_p90": float(np.percentile(lat["kernel"], 90)),
             "route_decode_p99": float(np.percentile(lat["kernel"], 99)),
+            "route_decode_p50_route_every_argument": float(np.percentile(lat["kernel_route"], 50)),
             "route_decode_p50_copy_gather": float(np.percentile(lat["copies"], 50)),
             "route_decode_pipelined_interval": float(pipe_ms),
             "route_decode_pipelined_interval_copy_gather": float(pipe_copy_ms),

@@ -10,6 +10,7 @@ from . import synth  # noqa: F401
 from ._lib import (  # noqa: F401
     Assembly,
     MSAError,
+    RouteCall,
     assemble,
     assemble_workspace_bytes,
     attend_workspace_bytes,
@@ -26,6 +27,6 @@ from ._lib import (  # noqa: F401
     sparse_decode_noalloc,
 )
 
-__all__ = ["Assembly", "MSAError", "assemble", "assemble_workspace_bytes", "attend_workspace_bytes", "bank_rows",
+__all__ = ["Assembly", "MSAError", "RouteCall", "assemble", "assemble_workspace_bytes", "attend_workspace_bytes", "bank_rows",
            "decode_workspace_bytes", "doc_map", "doc_map_bytes", "load", "pool_encode", "route",
            "route_workspace_bytes", "sparse_attend", "sparse_decode", "sparse_decode_noalloc", "synth"]

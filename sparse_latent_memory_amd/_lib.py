@@ -342,15 +342,13 @@ def assemble(topk_idx, doc_pool_off, assembly, workspace=None, stream=None):
     return assembly.mem_len
 
 
-def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, topk_score=None,
-          workspace=None, assembly=None, stream=None, prof_events=None, kr_layout="rows", n_pool=None,
-          doc_map=None):
-    """msa_route.  qr: [B, Tq, Hr, dr]; kr_pooled: the router bank in
-    `kr_layout` ("rows": [n_pool, Hr, dr]; "tiled": whole 16-row tiles,
-    n_pool given); doc_pool_off: int64 device [n_docs+1]; doc_map: optional,
-    doc_map(doc_pool_off, n_pool)'s output for these offsets.  Returns
-    (topk_idx, topk_score, doc_scores)."""
-    b, tq, hr, dr = qr.shape
+def _route_args(b, tq, hr, dr, q_dtype, dev, kr_pooled, doc_pool_off, top_k, doc_scores, topk_idx, topk_score,
+                workspace, assembly, stream, kr_layout, n_pool, doc_map, qr=None):
+    """RouteArgs (without the profiling events; without the query when qr is
+    None), with the checks msa_route's pointers need: outputs and buffers
+    the kernels write must hold what the call writes (checked first), then
+    every pointer's placement, the query's first.  Returns (args,
+    doc_scores, topk_idx, topk_score, workspace)."""
     lay = _layout_code(kr_layout)
     if n_pool is None:
         if lay == MSA_KR_TILED:
@@ -360,32 +358,91 @@ def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, to
         raise ValueError(f"kr_pooled holds {kr_pooled.numel()} elements, {n_pool} rows in the {kr_layout} layout "
                          f"need {bank_rows(n_pool, kr_layout) * hr * dr}")
     n_docs = doc_pool_off.numel() - 1
-    dev = qr.device
     if doc_scores is None:
         doc_scores = torch.empty((b, n_docs), dtype=torch.float32, device=dev)
     if topk_idx is None:
         topk_idx = torch.empty((b, top_k), dtype=torch.int32, device=dev)
     if topk_score is None:
         topk_score = torch.empty((b, top_k), dtype=torch.float32, device=dev)
+    for t, name, dt, n in ((doc_scores, "doc_scores", torch.float32, b * n_docs),
+                           (topk_idx, "topk_idx", torch.int32, b * top_k),
+                           (topk_score, "topk_score", torch.float32, b * top_k)):
+        if t.dtype != dt or t.numel() < n:
+            raise ValueError(f"{name} must be {dt} with at least {n} elements, got {t.dtype} with {t.numel()}")
     if workspace is None:
-        nbytes = route_workspace_bytes(qr.dtype, b, tq, hr, dr, n_docs, n_pool, top_k)
+        nbytes = route_workspace_bytes(q_dtype, b, tq, hr, dr, n_docs, n_pool, top_k)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
-    a = RouteArgs(dtype=dtype_code(qr.dtype), batch=b, q_tokens=tq, n_router_heads=hr, router_dim=dr,
-                  top_k=top_k, n_docs=n_docs, n_pool=n_pool, qr=_dptr(qr, "qr"), kr_pooled=_dptr(kr_pooled, "kr_pooled"),
+    a = RouteArgs(dtype=dtype_code(q_dtype), batch=b, q_tokens=tq, n_router_heads=hr, router_dim=dr,
+                  top_k=top_k, n_docs=n_docs, n_pool=n_pool, qr=None if qr is None else _dptr(qr, "qr"),
+                  kr_pooled=_dptr(kr_pooled, "kr_pooled"),
                   doc_pool_off=_dptr(doc_pool_off, "doc_pool_off"), doc_scores=_dptr(doc_scores, "doc_scores"),
                   topk_idx=_dptr(topk_idx, "topk_idx"), topk_score=_dptr(topk_score, "topk_score"),
-                  workspace=_dptr(workspace, "workspace"), workspace_bytes=workspace.numel(), kr_layout=lay)
+                  workspace=_dptr(workspace, "workspace"),
+                  workspace_bytes=workspace.numel() * workspace.element_size(), kr_layout=lay)
     if assembly is not None:
         _fill_assembly(a, assembly, stream)
-    if prof_events is not None:
-        a.prof_event_begin, a.prof_event_end = prof_events
     if doc_map is not None:
         if doc_map.numel() * doc_map.element_size() < doc_map_bytes(n_pool):
             raise ValueError(f"doc_map holds {doc_map.numel() * doc_map.element_size()} bytes, "
                              f"{doc_map_bytes(n_pool)} needed")
         a.doc_map = _dptr(doc_map, "doc_map")
+    return a, doc_scores, topk_idx, topk_score, workspace
+
+
+def route(qr, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None, topk_score=None,
+          workspace=None, assembly=None, stream=None, prof_events=None, kr_layout="rows", n_pool=None,
+          doc_map=None):
+    """msa_route.  qr: [B, Tq, Hr, dr]; kr_pooled: the router bank in
+    `kr_layout` ("rows": [n_pool, Hr, dr]; "tiled": whole 16-row tiles,
+    n_pool given); doc_pool_off: int64 device [n_docs+1]; doc_map: optional,
+    doc_map(doc_pool_off, n_pool)'s output for these offsets.  Returns
+    (topk_idx, topk_score, doc_scores)."""
+    b, tq, hr, dr = qr.shape
+    a, doc_scores, topk_idx, topk_score, _ = _route_args(b, tq, hr, dr, qr.dtype, qr.device, kr_pooled,
+                                                         doc_pool_off, top_k, doc_scores, topk_idx, topk_score,
+                                                         workspace, assembly, stream, kr_layout, n_pool, doc_map,
+                                                         qr=qr)
+    if prof_events is not None:
+        a.prof_event_begin, a.prof_event_end = prof_events
     _check(load().msa_route(ctypes.byref(a), _stream(stream)))
     return topk_idx, topk_score, doc_scores
+
+
+class RouteCall:
+    """msa_route with every argument but the query bound once, for serving
+    loops whose bank, outputs, workspace, document map and assembly stay the
+    same from call to call: route()'s checks and marshalling run here, once,
+    and each call checks the query (shape, dtype, placement) and sets its
+    pointer - about 1 us of host time before the first launch instead of
+    ~7 us.  The bound tensors are kept alive; an Assembly is bound as it is
+    at construction (tensors, mode, append flag).  Calls reuse one argument
+    block: one thread at a time.  Calling it returns (topk_idx, topk_score,
+    doc_scores)."""
+
+    def __init__(self, q_shape, q_dtype, kr_pooled, doc_pool_off, top_k, doc_scores=None, topk_idx=None,
+                 topk_score=None, workspace=None, assembly=None, kr_layout="rows", n_pool=None, doc_map=None):
+        b, tq, hr, dr = q_shape
+        dev = kr_pooled.device
+        (self._a, self.doc_scores, self.topk_idx, self.topk_score,
+         self.workspace) = _route_args(b, tq, hr, dr, q_dtype, dev, kr_pooled, doc_pool_off, top_k, doc_scores,
+                                       topk_idx, topk_score, workspace, assembly, None, kr_layout, n_pool, doc_map)
+        self._bound = (kr_pooled, doc_pool_off, doc_map, assembly)
+        self._shape = (b, tq, hr, dr)
+        self._dtype = q_dtype
+        self._copy_stream = None if assembly is None else assembly.copy_stream
+        self._assembly = assembly is not None
+        self._fn = load().msa_route
+
+    def __call__(self, qr, stream=None, prof_events=None):
+        if tuple(qr.shape) != self._shape or qr.dtype != self._dtype:
+            raise ValueError(f"qr must be {self._dtype} {list(self._shape)}, got {qr.dtype} {list(qr.shape)}")
+        a = self._a
+        a.qr = _dptr(qr, "qr")
+        if self._assembly:
+            a.copy_stream = _stream(self._copy_stream if self._copy_stream is not None else stream)
+        a.prof_event_begin, a.prof_event_end = prof_events if prof_events is not None else (None, None)
+        _check(self._fn(ctypes.byref(a), _stream(stream)))
+        return self.topk_idx, self.topk_score, self.doc_scores
 
 
 def doc_map_bytes(n_pool):

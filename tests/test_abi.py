@@ -389,6 +389,25 @@ def test_attend_workspace_size():
 
 
 
+def test_binding_checks_route_output_sizes():
+    """Route outputs that cannot hold what the call writes (B x n_docs scores,
+    B x k ids and scores) are refused by the binding before any call: the
+    library sees only their addresses."""
+    import sparse_latent_memory_amd as msa
+    bf = torch.bfloat16
+    qr = torch.zeros(2, 1, 8, 128, dtype=bf)
+    kr = torch.zeros(20, 8, 128, dtype=bf)
+    off = torch.tensor([0, 5, 20], dtype=torch.int64)
+    with pytest.raises(ValueError, match="doc_scores must be torch.float32 with at least 4"):
+        msa.route(qr, kr, off, 1, doc_scores=torch.zeros(3))
+    with pytest.raises(ValueError, match="doc_scores must be torch.float32"):
+        msa.route(qr, kr, off, 1, doc_scores=torch.zeros(4, dtype=torch.float64))
+    with pytest.raises(ValueError, match="topk_idx must be torch.int32 with at least 4"):
+        msa.route(qr, kr, off, 2, topk_idx=torch.zeros(2, 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="topk_score must be torch.float32 with at least 2"):
+        msa.route(qr, kr, off, 1, topk_score=torch.zeros(1))
+
+
 def test_binding_refuses_host_tensors_for_device_arguments():
     """A CPU tensor passed where the library takes device memory is refused
     by the binding before any call, with the argument named; pooled outputs

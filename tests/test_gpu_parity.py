@@ -892,6 +892,39 @@ def test_gather_is_byte_exact_in_rank_order(dtype, mode):
 
 
 @pytest.mark.parametrize("mode", ["kernel", "copies"])
+def test_route_call_matches_route(mode):
+    """RouteCall (every argument but the query bound once) gives route()'s
+    results bit for bit - scores, top-k and the gathered memory - with the
+    tiled bank, its document map and the assembly, for two queries in a
+    row; a query of another shape is refused before any launch."""
+    g = torch.Generator().manual_seed(23)
+    off, host_kv, kr = _bank_with_host_tier(g, 400, 9, 8, 128, torch.bfloat16)
+    n_pool = int(off[-1])
+    kt = synth.tile_router_bank(kr)
+    off_d = _dev(off)
+    dmap = msa.doc_map(off_d, n_pool)
+    k, cap = 12, 40
+    kw = dict(kr_layout="tiled", n_pool=n_pool, doc_map=dmap)
+    asm_a = msa.Assembly.allocate(host_kv, torch.as_tensor(off), 3, k, cap, DEV, copy_stream=torch.cuda.Stream(),
+                                  mode=mode)
+    asm_b = msa.Assembly.allocate(host_kv, torch.as_tensor(off), 3, k, cap, DEV, copy_stream=torch.cuda.Stream(),
+                                  mode=mode)
+    call = msa.RouteCall((3, 1, 8, 128), torch.bfloat16, kt, off_d, k, assembly=asm_b, **kw)
+    _say(f"route call ({mode}): 3 queries, top-{k}, two calls")
+    for step in range(2):
+        qr = _randn(g, 3, 1, 8, 128, dtype=torch.bfloat16).to(DEV)
+        idx_a, sc_a, dsc_a = msa.route(qr, kt, off_d, k, assembly=asm_a, **kw)
+        idx_b, sc_b, dsc_b = call(qr)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_a, idx_b) and torch.equal(sc_a.view(torch.int32), sc_b.view(torch.int32))
+        assert torch.equal(dsc_a.view(torch.int32), dsc_b.view(torch.int32))
+        assert torch.equal(asm_a.mem_len, asm_b.mem_len)
+        assert torch.equal(asm_a.mem_kv.view(torch.int16), asm_b.mem_kv.view(torch.int16))
+    with pytest.raises(ValueError, match="qr must be"):
+        call(_randn(g, 2, 1, 8, 128, dtype=torch.bfloat16).to(DEV))
+
+
+@pytest.mark.parametrize("mode", ["kernel", "copies"])
 def test_gather_append_mode(mode):
     g = torch.Generator().manual_seed(22)
     off, host_kv, kr = _bank_with_host_tier(g, 300, 6, 8, 128, torch.bfloat16)
