@@ -317,25 +317,32 @@ def main():
     calls = {name: msa.RouteCall(tuple(qrs[0].shape), qrs[0].dtype, bank, pool_off_d, k, doc_scores, topk_idx,
                                  topk_score, rws, assembly=a, **rkw)
              for name, a in (("kernel", asm), ("copies", asm_copies))}
+    # completion observed by polling an event (and, for comparison, by a
+    # blocking synchronise)
+    poll = CompletionPoll()
     lat = {}
-    for name, a, bound in (("kernel", asm, True), ("copies", asm_copies, True), ("kernel_route", asm, False)):
+    for name, a, bound, polled in (("kernel", asm, True, True), ("copies", asm_copies, True, True),
+                                   ("kernel_route", asm, False, True), ("kernel_sync", asm, True, False)):
         vals = []
         for i in range(W + K, n_steps):
             torch.cuda.synchronize()
             t = time.perf_counter()
             if bound:
-                calls[name](qrs[i], stream=stream)
+                calls[name.split("_")[0]](qrs[i], stream=stream)
             else:
                 msa.route(qrs[i], bank, pool_off_d, k, doc_scores, topk_idx, topk_score, rws, assembly=a,
                           stream=stream, **rkw)
             msa.sparse_decode(qs[i], a.mem_kv, a.mem_len, lk, lv, loc_len, pos, cfg.rope_theta, out, lse, dws,
                               stream=stream)
-            torch.cuda.synchronize()
+            if polled:
+                poll.wait(stream)
+            else:
+                torch.cuda.synchronize()
             vals.append((time.perf_counter() - t) * 1e3)
         lat[name] = np.array(vals)
     log(f"route+decode p50: kernel gather {np.median(lat['kernel']):.3f} ms "
-        f"(route() with every argument: {np.median(lat['kernel_route']):.3f} ms), "
-        f"copy gather {np.median(lat['copies']):.3f} ms")
+        f"(route() with every argument: {np.median(lat['kernel_route']):.3f} ms; waiting by synchronise: "
+        f"{np.median(lat['kernel_sync']):.3f} ms), copy gather {np.median(lat['copies']):.3f} ms")
 
     # pipelined steady state: consecutive queries alternate between two
     # streams with their own buffers (device-side assembly never waits on the
@@ -454,6 +461,7 @@ def main():
             "route_decode_p90": float(np.percentile(lat["kernel"], 90)),
             "route_decode_p99": float(np.percentile(lat["kernel"], 99)),
             "route_decode_p50_route_every_argument": float(np.percentile(lat["kernel_route"], 50)),
+            "route_decode_p50_synchronize": float(np.percentile(lat["kernel_sync"], 50)),
             "route_decode_p50_copy_gather": float(np.percentile(lat["copies"], 50)),
             "route_decode_pipelined_interval": float(pipe_ms),
             "route_decode_pipelined_interval_copy_gather": float(pipe_copy_ms),
@@ -469,6 +477,27 @@ def main():
 # --------------------------------------------------------------------------
 # supporting workloads (one JSON line each; not the headline line)
 # --------------------------------------------------------------------------
+
+class CompletionPoll:
+    """Waits for the work queued so far on a stream by polling a fence-free
+    HIP event (what a latency-bound caller does); a blocking synchronise adds
+    its wake-up, ~4 us after a half-millisecond wait."""
+
+    def __init__(self):
+        self.ev = HipEvents(1)
+        hip = self.ev.hip
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+        self.hip, self.e = hip, self.ev.pairs[0][0]
+
+    def wait(self, stream):
+        assert self.hip.hipEventRecord(self.e, ctypes.c_void_p(stream.cuda_stream)) == 0
+        while True:
+            st = self.hip.hipEventQuery(self.e)
+            if st == 0:
+                return
+            assert st == 600, f"hipEventQuery returned {st}"     # hipErrorNotReady
+
 
 class StreamEvents:
     """Event pairs on torch's current stream (the stream the library runs on here)."""
