@@ -101,15 +101,15 @@ constexpr int kWideWaves = 8;
 #ifndef MSA_WIDE_HEAD_OUTER // 1: heads outer when a workgroup walks few bank-tile groups (wide_tmax)
 #define MSA_WIDE_HEAD_OUTER 1
 #endif
-// Tiles per wave the heads-outer loop takes: as many (up to 3; 2 with two
-// heads, whose loop is unrolled; 1 for chunks of 8 query tiles) as fit its
+// Tiles per wave the heads-outer loop takes: as many (up to 3; 2 with two or
+// four heads, whose loops are unrolled; 1 for chunks of 8 query tiles) as fit its
 // registers - a head's query fragments (4 NM KS), per tile a bank-fragment
 // slot (4 KS) and 4 NM accumulators, and 4 NM more for the epilogue -
 // within a budget of 176 (the caps and the budget are where the compiled
 // instantiations stop spilling); 0: never.
 template <int HR, int NM, int KS>
 constexpr int wide_tmax() {
-  int t = NM >= 8 ? 1 : HR <= 2 ? 2 : 3;
+  int t = NM >= 8 ? 1 : HR <= 4 ? 2 : 3;
   while (t > 0 && 4 * NM * KS + 4 * KS * t + 4 * NM * (t + 1) > 176) --t;
   return t;
 }
@@ -286,29 +286,32 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
     int t0, t1;
     wide_chunk(L, c, &t0, &t1);
     const int nm = t1 - t0;
-    __syncthreads();                    // readers of the previous chunk are done
-    {
-      // The workgroups of one XCD that stage the same chunk start at
-      // different eighths of it: each line is fetched from memory by one and
-      // found in L2 by the others, instead of all of them waiting on the same
-      // misses together.
-      constexpr int NTH = kWideWaves * 64, NIT = (NM * NF * 64 + NTH - 1) / NTH;
-      const int rot = MSA_WIDE_STAGE_ROT ? ((L.n_chunks <= nwg ? stream : 0) & 7) * NIT / 8 : 0;
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int i = ((it + rot) % NIT) * NTH + (int)threadIdx.x;
-        if (i < NM * NF * 64) afrag[i] = i < nm * NF * 64 ? frag[(int64_t)t0 * NF * 64 + i] : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    __syncthreads();
     const int part = L.ppq > 1 ? c % L.ppq : 0;
+    const int64_t n_my = stream < n_groups ? (n_groups - 1 - stream) / S + 1 : 0;   // groups this workgroup walks
+    if (n_my == 0) continue;            // (uniform over the workgroup) no bank tile: nothing to stage or store
+    // The chunk into LDS by gfx950's loads straight to LDS (16 bytes a lane,
+    // no registers: the first bank loads are issued behind them and land
+    // while the chunk does), each wave 1 KiB fragments; tiles past the
+    // chunk's last copy its last one (their results are never stored).  The
+    // workgroups of one XCD that stage the same chunk start at different
+    // eighths of it: each line is fetched from memory by one and found in L2
+    // by the others, instead of all of them waiting on the same misses.
+    auto stage_chunk = [&]() {
+      constexpr int NFR = NM * NF;
+      const int rot = MSA_WIDE_STAGE_ROT ? ((L.n_chunks <= nwg ? stream : 0) & 7) * NFR / 8 : 0;
+      for (int f0 = wave; f0 < NFR; f0 += kWideWaves) {   // (uniform)
+        const int f = (f0 + rot) % NFR, mt = f / NF;
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void *>(frag + ((int64_t)t0 + min(mt, nm - 1)) * NF * 64 + (f % NF) * 64 + lane),
+            (__attribute__((address_space(3))) void *)(afrag + f * 64), 16, 0, 0);
+      }
+    };
+    __syncthreads();                    // readers of the previous chunk are done
 
     // Few bank tiles per wave (a small bank, many query tiles): heads outer,
     // so that a head's query fragments are read from LDS once and kept in
     // registers for all of the wave's tiles, whose accumulators stay live;
     // the per-head order of the sums is that of the tile loop below.
-    const int64_t n_my = stream < n_groups ? (n_groups - 1 - stream) / S + 1 : 0;   // groups this workgroup walks
-    if (n_my == 0) continue;            // (uniform over the workgroup) no bank tile: nothing to stage or store
     constexpr int TM = wide_tmax<HR, NM, KS>();
     if constexpr (HR > 1 && MSA_WIDE_HEAD_OUTER && TM > 0) {
       if (n_my <= TM) {
@@ -325,8 +328,10 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
         // last head, peeled, loads nothing.
         u32x4 fr[TM][KS];
         auto gj = [&](int j) { return stream + (int64_t)max(0, min(j, nj - 1)) * S; };
+        stage_chunk();
 #pragma unroll
         for (int j = 0; j < TM; ++j) load(gj(j), 0, fr[j]);
+        __syncthreads();                // the chunk in place (and the first bank fragments landed)
 #pragma unroll 1
         for (int h = 0; h < HR - 1; ++h) {
           u32x4 a[NM][KS];
@@ -363,8 +368,10 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
       }
     }
 
+    stage_chunk();
     u32x4 fa[KS], fb[KS];
     load(stream, 0, fa);
+    __syncthreads();                    // the chunk in place
     for (int64_t g = stream; g < n_groups; g += S) {
       const int64_t tile = g * kWideWaves + wave;
       const int64_t row = tile * 16 + col;
