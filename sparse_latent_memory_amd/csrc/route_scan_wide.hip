@@ -87,11 +87,12 @@ __global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict_
 // MFMAs against A-fragments read from LDS, scaled by the head's inverse norm.
 // Tiles of a chunk past its last real one are staged as zeros and their
 // results dropped, so the MFMA loop has no branches.
-// A workgroup that walks only a few groups of bank tiles (a small bank, many
-// query tiles: prefill routing) runs heads outer instead: each head's query
-// fragments are read from LDS once into registers and applied to all of the
-// wave's tiles, whose accumulators stay live, with one bank-fragment slot
-// per tile refilled as it is used.
+// A workgroup that walks only a few groups of bank tiles (a small bank:
+// prefill routing), or whose query tiles span several chunks, runs heads
+// outer instead, over batches of up to three of the wave's tiles: each
+// head's query fragments are read from LDS once per batch into registers
+// and applied to all of the batch's tiles, whose accumulators stay live,
+// with one bank-fragment slot per tile refilled as it is used.
 // When the query tiles span several chunks, chunks go to different
 // workgroups of one XCD that walk the same bank tiles in the same order, so
 // the bank is fetched from HBM about once and re-read from the XCD's L2 or
@@ -308,59 +309,68 @@ __global__ __launch_bounds__(kWideWaves * 64) void scan_wide_kernel(
     };
     __syncthreads();                    // readers of the previous chunk are done
 
-    // Few bank tiles per wave (a small bank, many query tiles): heads outer,
-    // so that a head's query fragments are read from LDS once and kept in
-    // registers for all of the wave's tiles, whose accumulators stay live;
-    // the per-head order of the sums is that of the tile loop below.
+    // Few bank tiles per wave (a small bank), or several chunks of query
+    // tiles (the tile loop would re-read a chunk's fragments from LDS for
+    // every bank tile): heads outer over batches of the wave's tiles, so that
+    // a head's query fragments are read from LDS once per batch and kept in
+    // registers, the batch's accumulators live; the per-head order of the
+    // sums is that of the tile loop below, which keeps the one-chunk scans
+    // of large banks (bound by HBM, their tiles streamed whole).
     constexpr int TM = wide_tmax<HR, NM, KS>();
     if constexpr (HR > 1 && MSA_WIDE_HEAD_OUTER && TM > 0) {
-      if (n_my <= TM) {
-        const int nj = (int)n_my;
-        f32x4 acc[TM][NM];
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-#pragma unroll
-          for (int mt = 0; mt < NM; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // one fragment slot per tile, refilled with the tile's next head as
-        // soon as it is used: TM loads in flight per wave.  No branches: slots
-        // past the workgroup's last group repeat the wave's last tile (its
-        // lines, already requested) and their results are never stored; the
-        // last head, peeled, loads nothing.
+      if (n_my <= TM || L.n_chunks > 1) {
+        // The wave's groups in batches of TM, heads outer within a batch.
+        // One fragment slot per tile, refilled with the tile's next head as
+        // soon as it is used, and in the batch's last head with the next
+        // batch's first: TM loads in flight per wave throughout.  No
+        // branches: slots past the workgroup's last group repeat its last
+        // group (lines already requested), their results never stored.
         u32x4 fr[TM][KS];
-        auto gj = [&](int j) { return stream + (int64_t)max(0, min(j, nj - 1)) * S; };
+        auto gof = [&](int64_t j) { return stream + (j < n_my ? j : n_my - 1) * S; };
         stage_chunk();
 #pragma unroll
-        for (int j = 0; j < TM; ++j) load(gj(j), 0, fr[j]);
+        for (int j = 0; j < TM; ++j) load(gof(j), 0, fr[j]);
         __syncthreads();                // the chunk in place (and the first bank fragments landed)
+        for (int64_t jb = 0; jb < n_my; jb += TM) {   // (uniform)
+          f32x4 acc[TM][NM];
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+#pragma unroll
+            for (int mt = 0; mt < NM; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-        for (int h = 0; h < HR - 1; ++h) {
-          u32x4 a[NM][KS];
-          read_a(h, a);
+          for (int h = 0; h < HR - 1; ++h) {
+            u32x4 a[NM][KS];
+            read_a(h, a);
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+              __builtin_amdgcn_sched_barrier(0);
+              head_mma(a, fr[j], acc[j]);
+              load(gof(jb + j), h + 1, fr[j]);
+            }
+          }
+          {
+            u32x4 a[NM][KS];
+            read_a(HR - 1, a);
+#pragma unroll
+            for (int j = 0; j < TM; ++j) {
+              __builtin_amdgcn_sched_barrier(0);
+              head_mma(a, fr[j], acc[j]);
+              load(gof(jb + TM + j), 0, fr[j]);   // (after the last batch: valid, unused)
+            }
+          }
 #pragma unroll
           for (int j = 0; j < TM; ++j) {
-            __builtin_amdgcn_sched_barrier(0);
-            head_mma(a, fr[j], acc[j]);
-            load(gj(j), h + 1, fr[j]);
-          }
-        }
-        {
-          u32x4 a[NM][KS];
-          read_a(HR - 1, a);
-#pragma unroll
-          for (int j = 0; j < TM; ++j) head_mma(a, fr[j], acc[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          if (j < nj) {
-            const int64_t tile = (stream + (int64_t)j * S) * kWideWaves + wave;
-            const int64_t row = tile * 16 + col;
-            if (L.tok1) {
-              const int64_t tc = tile < n_tiles ? tile : n_tiles - 1;
-              const uint32_t bits = tile_bits[tc];
-              const int32_t tdoc = tile_doc[tc];
-              if (tile < n_tiles) epilogue_docs(t0, nm, tile, bits, tdoc, acc[j]);   // (wave-uniform)
-            } else if (row < n_pool) {
-              epilogue(t0, nm, part, row, acc[j]);
+            if (jb + j < n_my) {
+              const int64_t tile = (stream + (jb + j) * S) * kWideWaves + wave;
+              const int64_t row = tile * 16 + col;
+              if (L.tok1) {
+                const int64_t tc = tile < n_tiles ? tile : n_tiles - 1;
+                const uint32_t bits = tile_bits[tc];
+                const int32_t tdoc = tile_doc[tc];
+                if (tile < n_tiles) epilogue_docs(t0, nm, tile, bits, tdoc, acc[j]);   // (wave-uniform)
+              } else if (row < n_pool) {
+                epilogue(t0, nm, part, row, acc[j]);
+              }
             }
           }
         }
