@@ -302,23 +302,26 @@ def test_route_more_query_chunks_than_workgroups(b, tq):
     _route_check(kr, off, qr, 8, f"wide chunks B{b} Tq{tq}")
 
 
-def test_route_heads_outer_and_tile_loops_in_one_launch():
-    """A 256-token query (four chunks of query tiles) over a bank of 1,538
-    tiles (193 groups of 8): on a 256-CU device 64 workgroups walk each
-    chunk's groups, so workgroups 1..63 walk three groups (the heads-outer
-    loop, three tiles per wave) and workgroup 0 walks four (the tile loop),
-    in one launch; row-major and tiled banks identical, and checked against
-    the oracle."""
-    g = torch.Generator().manual_seed(4242)
-    rows = np.full(2460, 10, dtype=np.int64)                 # 24,600 rows: 1,537 whole tiles and half of one
+@pytest.mark.parametrize("b,tq,n_docs", [(1, 256, 2460), (64, 1, 10240)])
+def test_route_heads_outer_and_tile_loops_in_one_launch(b, tq, n_docs):
+    """Workgroups that take the wide scan's loops differently, in one launch
+    on a 256-CU device.  One 256-token query (four chunks of query tiles,
+    64 workgroups per chunk) over 24,600 rows (193 groups of 8 tiles):
+    workgroups 1..63 walk three groups (one heads-outer batch), workgroup 0
+    four (batches of three and one).  64 one-token queries (one chunk, 256
+    workgroups) over 102,400 rows (800 groups): workgroups 0..31 walk four
+    groups (the tile loop), the others three (heads outer).  Row-major and
+    tiled banks identical, and checked against the oracle."""
+    g = torch.Generator().manual_seed(4242 + b)
+    rows = np.full(n_docs, 10, dtype=np.int64)
     off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
     kr = _randn(g, int(off[-1]), 8, 128, dtype=torch.bfloat16).to(DEV)
-    qr = _randn(g, 1, 256, 8, 128, dtype=torch.bfloat16).to(DEV)
-    _say(f"route: heads-outer and tile loops in one launch, {int(off[-1])} rows, Tq=256")
-    idx, dsc = _route_both_layouts(qr, kr, off, 16, "heads-outer boundary")
+    qr = _randn(g, b, tq, 8, 128, dtype=torch.bfloat16).to(DEV)
+    _say(f"route: heads-outer and tile loops in one launch, {int(off[-1])} rows, B={b} Tq={tq}")
+    idx, dsc = _route_both_layouts(qr, kr, off, 16, f"loop boundary B={b} Tq={tq}")
     ref = oracle.doc_scores(np64(qr), np64(kr), off)
-    check_scores(np64(dsc), ref, "heads-outer boundary vs oracle")
-    check_topk(np64(idx), ref, 16, "heads-outer boundary vs oracle")
+    check_scores(np64(dsc), ref, f"loop boundary B={b} Tq={tq} vs oracle")
+    check_topk(np64(idx), ref, 16, f"loop boundary B={b} Tq={tq} vs oracle")
 
 
 def test_route_prefill_config_full_size():
