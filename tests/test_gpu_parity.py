@@ -930,6 +930,103 @@ def test_route_call_matches_route(mode):
 
 
 @pytest.mark.parametrize("mode", ["kernel", "copies"])
+def test_two_stream_schedule_matches_one_stream(mode):
+    """The serving schedule the benchmark's pipelined pass runs: consecutive
+    queries alternate between two streams, each with its own outputs,
+    workspaces and memory, so one query's selection, assembly and decode run
+    beside the next query's bank scan (kernel mode: msa_route with the
+    assembly; copies: msa_route without it, then msa_assemble for the
+    previous query, whose copies cross the host link while the next query is
+    scored).  Scores, top-k, the assembled memory and the decode output equal
+    those of the same queries run one at a time on one stream, bit for bit,
+    and every query's memory and decode match the oracle."""
+    g = torch.Generator().manual_seed(31)
+    off, host_kv, kr = _bank_with_host_tier(g, 3000, 9, 8, 128, torch.bfloat16)
+    n_docs, n_pool = len(off) - 1, int(off[-1])
+    kt = synth.tile_router_bank(kr)
+    off_d, off_h = _dev(off), torch.as_tensor(off)
+    dmap = msa.doc_map(off_d, n_pool)
+    k, cap, n_q, hq, hkv, d, t_loc = 16, 144, 6, 32, 8, 128, 300
+    kw = dict(kr_layout="tiled", n_pool=n_pool, doc_map=dmap)
+    lk = _randn(g, 1, t_loc, hkv, d, dtype=torch.bfloat16)
+    lv = _randn(g, 1, t_loc, hkv, d, dtype=torch.bfloat16)
+    lk_d, lv_d = _dev(lk), _dev(lv)
+    loc_len = torch.full((1,), t_loc, dtype=torch.int32, device=DEV)
+    pos = torch.full((1,), k, dtype=torch.int32, device=DEV)
+    qrs = [_randn(g, 1, 1, 8, 128, dtype=torch.bfloat16).to(DEV) for _ in range(n_q)]
+    qs = [_randn(g, 1, hq, d, dtype=torch.bfloat16).to(DEV) for _ in range(n_q)]
+    rws_bytes = msa.route_workspace_bytes(torch.bfloat16, 1, 1, 8, 128, n_docs, n_pool, k)
+    dws_bytes = msa.decode_workspace_bytes(1, hq, d, cap, t_loc)
+
+    def lane(stream):
+        return {"s": stream, "asm": msa.Assembly.allocate(host_kv, off_h, 1, k, cap, DEV,
+                                                          copy_stream=torch.cuda.Stream(), mode=mode),
+                "rws": torch.empty(rws_bytes, dtype=torch.uint8, device=DEV),
+                "dws": torch.empty(dws_bytes, dtype=torch.uint8, device=DEV),
+                "dsc": torch.empty(1, n_docs, dtype=torch.float32, device=DEV),
+                "idx": torch.empty(1, k, dtype=torch.int32, device=DEV),
+                "sc": torch.empty(1, k, dtype=torch.float32, device=DEV),
+                "out": torch.empty(1, hq, d, dtype=torch.bfloat16, device=DEV),
+                "lse": torch.empty(1, hq, dtype=torch.float32, device=DEV)}
+
+    def route(i, L, assembled):
+        msa.route(qrs[i], kt, off_d, k, L["dsc"], L["idx"], L["sc"], L["rws"],
+                  assembly=L["asm"] if assembled else None, stream=L["s"], **kw)
+
+    def finish(i, L, assemble, res):
+        if assemble:
+            msa.assemble(L["idx"], off_d, L["asm"], stream=L["s"])
+        msa.sparse_decode(qs[i], L["asm"].mem_kv, L["asm"].mem_len, lk_d, lv_d, loc_len, pos, THETA, L["out"],
+                          L["lse"], L["dws"], stream=L["s"])
+        with torch.cuda.stream(L["s"]):    # this query's results, before the lane's next query
+            res[i] = [t.clone() for t in (L["dsc"], L["idx"], L["sc"], L["asm"].mem_len, L["asm"].mem_kv,
+                                          L["out"], L["lse"])]
+
+    _say(f"two-stream schedule ({mode}): {n_q} queries over {n_docs} documents, top-{k}, cap {cap}")
+    main = torch.cuda.current_stream()
+    one, two = {}, {}
+    solo = lane(main)
+    for i in range(n_q):                   # one at a time on one stream
+        route(i, solo, mode == "kernel")
+        finish(i, solo, mode == "copies", one)
+        torch.cuda.synchronize()
+    lanes = [lane(main), lane(torch.cuda.Stream())]
+    prev = None
+    for n in range(n_q):                   # alternating lanes, no synchronisation between queries
+        L = lanes[n % 2]
+        route(n, L, mode == "kernel")
+        if mode == "kernel":
+            finish(n, L, False, two)
+        else:
+            if prev is not None:
+                finish(*prev, True, two)
+            prev = (n, L)
+    if prev is not None:
+        finish(*prev, True, two)
+    torch.cuda.synchronize()
+
+    bits = lambda t: t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)  # noqa: E731
+    src = host_kv.view(torch.int16).numpy()
+    for i in range(n_q):
+        dsc1, idx1, sc1, len1, mem1, out1, lse1 = one[i]
+        dsc2, idx2, sc2, len2, mem2, out2, lse2 = two[i]
+        m = int(len1[0])
+        assert torch.equal(bits(dsc1), bits(dsc2)) and torch.equal(idx1, idx2) and torch.equal(bits(sc1), bits(sc2))
+        assert torch.equal(len1, len2) and torch.equal(bits(mem1[:, :m]), bits(mem2[:, :m]))
+        assert torch.equal(bits(out1), bits(out2)) and torch.equal(bits(lse1), bits(lse2)), f"query {i}"
+        ref_mem, ref_len, _ = oracle.assemble(src, off, np64(idx2), cap)
+        assert np.array_equal(np64(len2), ref_len)
+        assert np.array_equal(bits(mem2).cpu().numpy()[:, :m], ref_mem[:, :m])
+        ro, _ = oracle.decode(np64(qs[i]), np64(mem2), np64(len2), np64(lk), np64(lv), [t_loc], [k], THETA, None,
+                              storage(torch.bfloat16))
+        check_decode(np64(out2), ro, torch.bfloat16, f"two-stream decode, query {i}")
+    # the routing itself against the oracle for the first query
+    ref_scores = oracle.doc_scores(np64(qrs[0]), np64(kr), off)
+    check_scores(np64(two[0][0]), ref_scores, "two-stream doc scores")
+    check_topk(np64(two[0][1]), ref_scores, k, "two-stream top-k")
+
+
+@pytest.mark.parametrize("mode", ["kernel", "copies"])
 def test_gather_append_mode(mode):
     g = torch.Generator().manual_seed(22)
     off, host_kv, kr = _bank_with_host_tier(g, 300, 6, 8, 128, torch.bfloat16)
