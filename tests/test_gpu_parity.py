@@ -502,6 +502,36 @@ def test_route_top_k_bound_when_block_maxima_tie():
     _route_both_layouts(qr, kr, off, 16, "tied block maxima, tiled")
 
 
+@pytest.mark.parametrize("k", [16, 4096])
+def test_route_top_k_over_more_than_4096_blocks(k):
+    """1,100,000 one-row documents (4,297 blocks of 256, more than the block
+    bound orders): the selection takes its radix select over every document
+    key, at k = 16 and at the largest k the library takes (4,096), and with
+    the device-side assembly at that k the copy plan drops every rank from the
+    first document that no longer fits (capacity 3,000 rows); scores, top-k,
+    order and the gathered memory against the oracle."""
+    g = torch.Generator().manual_seed(4100 + k)
+    n_docs, cap = 1_100_000, 3000
+    off = np.arange(n_docs + 1, dtype=np.int64)
+    kr = torch.randn(n_docs, 1, 128, generator=g).to(torch.bfloat16).to(DEV)
+    qr = torch.randn(2, 1, 1, 128, generator=g).to(torch.bfloat16).to(DEV)
+    host_kv = torch.randn(n_docs, 2, 1, 64, generator=g).to(torch.bfloat16).pin_memory()
+    _say(f"route: {n_docs} one-row documents, top-{k}, radix selection, assembly cap {cap}")
+    idx, ref = _route_check(kr, off, qr, k, f"{n_docs} documents, top-{k}")
+    asm = msa.Assembly.allocate(host_kv, torch.as_tensor(off), 2, k, cap, DEV, mode="kernel")
+    idx_a, _, _ = msa.route(qr, kr, _dev(off), k, assembly=asm)
+    torch.cuda.synchronize()
+    assert np.array_equal(np64(idx_a), idx)
+    src = host_kv.view(torch.int16).numpy()
+    ref_mem, ref_len, ref_taken = oracle.assemble(src, off, idx, cap)
+    assert np.array_equal(np64(asm.mem_len), ref_len)
+    assert ref_taken.tolist() == [min(k, cap)] * 2
+    got = asm.mem_kv.view(torch.int16).cpu().numpy()
+    for b in range(2):
+        assert np.array_equal(got[b, :ref_len[b]], ref_mem[b, :ref_len[b]]), f"memory of query {b}"
+    _route_both_layouts(qr, kr, off, k, f"{n_docs} documents, top-{k}, tiled")
+
+
 def test_route_all_documents_and_degenerate_rows():
     g = torch.Generator().manual_seed(6)
     kr, off = _ragged_bank(g, 37, 3, 8, 128, torch.bfloat16)
