@@ -836,6 +836,16 @@ def test_attend_prefill_routing_layer_shape():
     _attend_check(1, 256, 32, 8, 128, 256, 2048, [170], [2048], [16], "prefill", mem_scale=8.0, seed=5)
 
 
+@pytest.mark.parametrize("tq,t_loc", [(2048, 2048), (1000, 1500)])
+def test_attend_long_prefill_blocks(tq, t_loc):
+    """Long prefill blocks: every local token a query token (2,048 tokens,
+    512 query tiles per KV head) and 1,000 of 1,500; causal over the whole
+    block, ~170 memory rows, GQA 32/8 x 128, against the oracle."""
+    _say(f"attend: Tq={tq} prefill over local {t_loc}, 32/8 x 128, memory 170 rows")
+    _attend_check(1, tq, 32, 8, 128, 256, t_loc, [170], [t_loc], [16], f"prefill Tq={tq}", mem_scale=4.0,
+                  seed=tq)
+
+
 def test_attend_interleave_batch_shape():
     _say("attend: 64 queries x 1 token, memory 600 rows, local 1024")
     _attend_check(64, 1, 32, 8, 128, 700, 1024, list(range(540, 604)), [1024] * 64, [8] * 64, "batch 64",
