@@ -302,7 +302,7 @@ def test_route_more_query_chunks_than_workgroups(b, tq):
     _route_check(kr, off, qr, 8, f"wide chunks B{b} Tq{tq}")
 
 
-@pytest.mark.parametrize("b,tq,n_docs", [(1, 256, 2460), (64, 1, 10240), (1, 256, 8200)])
+@pytest.mark.parametrize("b,tq,n_docs", [(1, 256, 2460), (64, 1, 10240), (1, 256, 8200), (256, 1, 10240)])
 def test_route_heads_outer_and_tile_loops_in_one_launch(b, tq, n_docs):
     """Workgroups that take the wide scan's loops differently, in one launch
     on a 256-CU device.  One 256-token query (four chunks of query tiles,
@@ -312,8 +312,10 @@ def test_route_heads_outer_and_tile_loops_in_one_launch(b, tq, n_docs):
     10 or 11 groups in batches of three and a shorter last one.  64
     one-token queries (one chunk, 256 workgroups) over 102,400 rows (800
     groups): workgroups 0..31 walk four groups (the tile loop), the others
-    three (heads outer).  Row-major and tiled banks identical, and checked
-    against the oracle."""
+    three (heads outer).  256 one-token queries (four chunks, 64 workgroups
+    per chunk) over the same rows: 12 or 13 groups per workgroup in
+    heads-outer batches, each run's per-document maxima stored per chunk.
+    Row-major and tiled banks identical, and checked against the oracle."""
     g = torch.Generator().manual_seed(4242 + b)
     rows = np.full(n_docs, 10, dtype=np.int64)
     off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
