@@ -221,7 +221,7 @@ def main():
         write_traffic_record(*args.write_traffic_record)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the bank is held whole in one GPU's HBM); "
+        print("bench.py: this benchmark runs on one GPU only (the bank is held whole in one GPU's HBM); "
               "multi-GPU runs are not supported", file=sys.stderr)
         sys.exit(2)
 
