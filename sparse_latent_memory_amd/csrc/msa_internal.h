@@ -126,6 +126,8 @@ hipError_t launch_scan_narrow(const msa_route_args &a, const RouteWs &ws, hipStr
 hipError_t launch_prep_unit(const msa_route_args &a, float *qhat, hipStream_t s);
 // bf16 query fragments and the MFMA scan for more than 8 tokens
 hipError_t launch_prep_wide(const msa_route_args &a, const float *qhat, u32x4 *frag, hipStream_t s);
+// the same fragments straight from bf16 queries (norms included), one launch
+hipError_t launch_prep_wide_direct(const msa_route_args &a, u32x4 *frag, hipStream_t s);
 hipError_t launch_scan_wide(const msa_route_args &a, const u32x4 *frag, const RouteWs &ws, hipStream_t s);
 // fp32 (any token count): one wave per bank row
 hipError_t launch_scan_valu(const msa_route_args &a, const float *qhat, float *row_score, hipStream_t s);

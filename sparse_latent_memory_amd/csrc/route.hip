@@ -10,7 +10,7 @@
 //    head-mean cosine of pooled row j:
 //      bf16, at most 8 tokens   scan_mfma_kernel (route_scan.hip), query prep
 //                               fused in;
-//      bf16, more tokens        prep_unit + prep_wide + scan_wide_kernel
+//      bf16, more tokens        prep_wide_direct + scan_wide_kernel
 //                               (route_scan_wide.hip);
 //      fp32                     prep_unit + scan_valu_kernel;
 //  * selection (route_select.hip): per-document max, exact top-k, and with
@@ -22,6 +22,9 @@
 
 #ifndef MSA_ROUTE_NARROW_DOCS   // 1: one-token batches of up to 8 queries also take the document path
 #define MSA_ROUTE_NARROW_DOCS 1
+#endif
+#ifndef MSA_ROUTE_PREP_DIRECT   // 1: the wide scan's query fragments in one launch from the bf16 queries
+#define MSA_ROUTE_PREP_DIRECT 1
 #endif
 
 namespace msa {
@@ -69,7 +72,7 @@ size_t route_ws_layout(int32_t dtype, int32_t batch, int32_t q_tokens, int32_t h
   const size_t o_tb = off;
   if (docs) off = align256(off + sizeof(uint32_t) * (size_t)n_tiles);
   const size_t o_q = off;
-  if (!narrow_path(dtype, M, hr, dr)) off = align256(off + sizeof(float) * (size_t)M * hr * dr);
+  if (!narrow && !(wide && MSA_ROUTE_PREP_DIRECT)) off = align256(off + sizeof(float) * (size_t)M * hr * dr);
   const size_t o_w = off;
   if (wide) off = align256(off + sizeof(u32x4) * 64 * (size_t)hr * (dr / 32) * wide_tiles(batch, q_tokens));
   const size_t o_bm = off;
@@ -105,14 +108,19 @@ hipError_t launch_route(const msa_route_args &a, const RouteWs &ws, const void *
       return e;
     e = launch_scan_narrow(a, ws, s);
   } else {
-    if ((e = launch_prep_unit(a, ws.qhat, s)) != hipSuccess) return e;
     if (wide_path(a.dtype, M, a.n_router_heads, a.router_dim)) {
+#if MSA_ROUTE_PREP_DIRECT
+      if ((e = launch_prep_wide_direct(a, ws.wide_frag, s)) != hipSuccess) return e;
+#else
+      if ((e = launch_prep_unit(a, ws.qhat, s)) != hipSuccess) return e;
       if ((e = launch_prep_wide(a, ws.qhat, ws.wide_frag, s)) != hipSuccess) return e;
+#endif
       if (ws.qstride > 0 && !ws.map_given &&
           (e = launch_doc_map(a.doc_pool_off, a.n_docs, a.n_pool, ws.tile_doc, ws.tile_bits, s)) != hipSuccess)
         return e;
       e = launch_scan_wide(a, ws.wide_frag, ws, s);
     } else {
+      if ((e = launch_prep_unit(a, ws.qhat, s)) != hipSuccess) return e;
       e = launch_scan_valu(a, ws.qhat, ws.row_score, s);
     }
   }

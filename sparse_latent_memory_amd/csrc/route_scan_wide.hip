@@ -78,6 +78,53 @@ __global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict_
   }
 }
 
+// The same fragments straight from the bf16 queries, one launch instead of
+// prep_unit + prep_wide: each thread sums the squares of its (token, head)
+// row itself (the row's 16 threads read it from L2) and writes its 8
+// elements scaled by 1 / (max(|q|, eps) Hr), rounded to bf16 once.
+__global__ __launch_bounds__(256) void prep_wide_direct_kernel(const uint16_t *__restrict__ qr,
+                                                               u32x4 *__restrict__ frag, int B, int Tq, int Hr,
+                                                               int dr, int n_mt) {
+  const int KS = dr / 32, NF = Hr * KS;
+  const int mtq = (Tq + 15) / 16;
+  const int64_t n = (int64_t)n_mt * NF * 64;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(idx & 63);
+    const int f = (int)((idx >> 6) % NF);
+    const int mt = (int)((idx >> 6) / NF);
+    const int h = f / KS, s = f % KS, r = l & 15;
+    int m = -1;                               // query token of this row, or none
+    if (Tq == 1) {
+      const int b = mt * 16 + r;
+      if (b < B) m = b;
+    } else {
+      const int b = mt / mtq;
+      const int t = min((mt % mtq) * 16 + r, Tq - 1);
+      m = b * Tq + t;
+    }
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (m >= 0) {
+      const uint16_t *row = qr + ((int64_t)m * Hr + h) * dr;
+      float ss = 0.f;
+      for (int i = 0; i < dr; i += 8) {
+        float x[8];
+        Elt<uint16_t>::unpack(ld16(row + i), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      }
+      const float scale = 1.0f / (fmaxf(sqrtf(ss), kEps) * (float)Hr);
+      float x[8];
+      Elt<uint16_t>::unpack(ld16(row + 32 * s + 8 * (l >> 4)), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e >> 1] |= (uint32_t)f32_to_bf16(x[e] * scale) << (16 * (e & 1));
+    }
+    u32x4 o;
+    o.x = w[0]; o.y = w[1]; o.z = w[2]; o.w = w[3];
+    frag[idx] = o;
+  }
+}
+
 // One workgroup of 8 waves per CU (two per SIMD).  The workgroup keeps one
 // chunk of NM query M-tiles in LDS (at most 128 KiB) for the whole launch;
 // every wave streams 16-row bank tiles from HBM one head at a time, loading
@@ -542,6 +589,15 @@ hipError_t launch_prep_wide(const msa_route_args &a, const float *qhat, u32x4 *f
   const int64_t n = (int64_t)n_mt * a.n_router_heads * (a.router_dim / 32) * 64;
   hipLaunchKernelGGL(prep_wide_kernel, dim3((int)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s, qhat,
                      frag, a.batch, a.q_tokens, a.n_router_heads, a.router_dim, n_mt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep_wide_direct(const msa_route_args &a, u32x4 *frag, hipStream_t s) {
+  const int n_mt = wide_tiles(a.batch, a.q_tokens);
+  const int64_t n = (int64_t)n_mt * a.n_router_heads * (a.router_dim / 32) * 64;
+  hipLaunchKernelGGL(prep_wide_direct_kernel, dim3((int)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t *>(a.qr), frag, a.batch, a.q_tokens, a.n_router_heads,
+                     a.router_dim, n_mt);
   return hipGetLastError();
 }
 
