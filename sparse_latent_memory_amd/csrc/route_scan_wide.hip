@@ -82,10 +82,12 @@ __global__ __launch_bounds__(256) void prep_wide_kernel(const float *__restrict_
 // prep_unit + prep_wide: each thread sums the squares of its (token, head)
 // row itself (the row's 16 threads read it from L2) and writes its 8
 // elements scaled by 1 / (max(|q|, eps) Hr), rounded to bf16 once.
+template <int DR>
 __global__ __launch_bounds__(256) void prep_wide_direct_kernel(const uint16_t *__restrict__ qr,
                                                                u32x4 *__restrict__ frag, int B, int Tq, int Hr,
-                                                               int dr, int n_mt) {
-  const int KS = dr / 32, NF = Hr * KS;
+                                                               int n_mt) {
+  constexpr int KS = DR / 32;
+  const int NF = Hr * KS;
   const int mtq = (Tq + 15) / 16;
   const int64_t n = (int64_t)n_mt * NF * 64;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
@@ -105,17 +107,21 @@ __global__ __launch_bounds__(256) void prep_wide_direct_kernel(const uint16_t *_
     }
     uint32_t w[4] = {0, 0, 0, 0};
     if (m >= 0) {
-      const uint16_t *row = qr + ((int64_t)m * Hr + h) * dr;
+      const uint16_t *row = qr + ((int64_t)m * Hr + h) * DR;
+      u32x4 v[DR / 8];                        // the whole row in flight at once
+#pragma unroll
+      for (int i = 0; i < DR / 8; ++i) v[i] = ld16(row + 8 * i);
       float ss = 0.f;
-      for (int i = 0; i < dr; i += 8) {
+#pragma unroll
+      for (int i = 0; i < DR / 8; ++i) {
         float x[8];
-        Elt<uint16_t>::unpack(ld16(row + i), x);
+        Elt<uint16_t>::unpack(v[i], x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
       }
       const float scale = 1.0f / (fmaxf(sqrtf(ss), kEps) * (float)Hr);
       float x[8];
-      Elt<uint16_t>::unpack(ld16(row + 32 * s + 8 * (l >> 4)), x);
+      Elt<uint16_t>::unpack(ld16(row + 32 * s + 8 * (l >> 4)), x);   // this lane's 8 elements (a cached line)
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[e >> 1] |= (uint32_t)f32_to_bf16(x[e] * scale) << (16 * (e & 1));
     }
@@ -595,9 +601,14 @@ hipError_t launch_prep_wide(const msa_route_args &a, const float *qhat, u32x4 *f
 hipError_t launch_prep_wide_direct(const msa_route_args &a, u32x4 *frag, hipStream_t s) {
   const int n_mt = wide_tiles(a.batch, a.q_tokens);
   const int64_t n = (int64_t)n_mt * a.n_router_heads * (a.router_dim / 32) * 64;
-  hipLaunchKernelGGL(prep_wide_direct_kernel, dim3((int)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t *>(a.qr), frag, a.batch, a.q_tokens, a.n_router_heads,
-                     a.router_dim, n_mt);
+  const dim3 grid((int)std::min<int64_t>((n + 255) / 256, 4096));
+  const uint16_t *qr = reinterpret_cast<const uint16_t *>(a.qr);
+  if (a.router_dim == 64)
+    hipLaunchKernelGGL(prep_wide_direct_kernel<64>, grid, dim3(256), 0, s, qr, frag, a.batch, a.q_tokens,
+                       a.n_router_heads, n_mt);
+  else
+    hipLaunchKernelGGL(prep_wide_direct_kernel<128>, grid, dim3(256), 0, s, qr, frag, a.batch, a.q_tokens,
+                       a.n_router_heads, n_mt);
   return hipGetLastError();
 }
 
